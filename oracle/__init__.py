@@ -1,0 +1,194 @@
+"""CPU oracle for the MoE layer hot path -- TEST INFRASTRUCTURE ONLY.
+
+Only the test-suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never does, and the two share no code.
+
+The arithmetic lives in ``moe_oracle.c`` (plain C, fp64); this module only
+builds/loads it and marshals numpy arrays through ctypes.  The function
+docstrings say which step of the layer each call is; the C file's header
+cites the passages of the pages each step follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB = os.path.join(_HERE, "libmoe_oracle.so")
+
+F32 = 0
+BF16 = 1
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (IEEE double, no contraction, OpenMP)."""
+    if force or not os.path.exists(_LIB):
+        cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+               "-shared", "-fPIC", _SRC, "-o", _LIB + ".tmp", "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I64, I32 = ctypes.c_int64, ctypes.c_int
+        lib.orc_round_to_bf16.argtypes = [ctypes.c_double]
+        lib.orc_round_to_bf16.restype = ctypes.c_double
+        lib.orc_route.argtypes = [I64, I32, I32, P, P, P]
+        lib.orc_counts_offsets.argtypes = [I64, I32, I32, I32, P, P, P, P]
+        lib.orc_permutation.argtypes = [I64, I32, I32, I32, P, P, P, P]
+        lib.orc_dispatch.argtypes = [I64, I32, I32, I32, P, P, P]
+        lib.orc_ffn_rows.argtypes = [I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, I64, P, P, P]
+        lib.orc_combine_tokens.argtypes = [I32, I32, I64, P, P, P]
+        lib.orc_moe_layer.argtypes = [I64, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, I64, P,
+                                      P, P, P, P, P, P, P, P, P]
+        lib.orc_num_threads.argtypes = []
+        for name in ("orc_route", "orc_counts_offsets", "orc_permutation", "orc_dispatch",
+                     "orc_ffn_rows", "orc_combine_tokens", "orc_moe_layer", "orc_num_threads"):
+            getattr(lib, name).restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _p(a):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what} rejected its arguments (rc={rc})")
+
+
+def _dtype_code(arr):
+    if arr.dtype == np.float32:
+        return F32
+    if arr.dtype == np.uint16:
+        return BF16
+    raise TypeError("oracle takes float32 arrays or bf16 bit patterns as uint16")
+
+
+def round_to_bf16(v: float) -> float:
+    """The oracle's own double -> bf16 (round to nearest even) rounding."""
+    return _load().orc_round_to_bf16(float(v))
+
+
+def num_threads() -> int:
+    return _load().orc_num_threads()
+
+
+def route(logits, k):
+    """Step 1: top-k indices (descending, ties to the lower index) and weights."""
+    logits = _c(logits, np.float32)
+    M, E = logits.shape
+    idx = np.empty((M, k), np.int32)
+    w = np.empty((M, k), np.float32)
+    _check(_load().orc_route(M, E, k, _p(logits), _p(idx), _p(w)), "route")
+    return idx, w
+
+
+def counts_offsets(topk_idx, E, S=1, src_block=None):
+    """Step 2: per-(source block, expert) counts and the exclusive prefix sum."""
+    topk_idx = _c(topk_idx, np.int32)
+    src_block = _c(src_block, np.int32)
+    M, k = topk_idx.shape
+    counts = np.empty(S * E, np.int32)
+    offsets = np.empty(S * E + 1, np.int32)
+    _check(_load().orc_counts_offsets(M, E, k, S, _p(topk_idx), _p(src_block), _p(counts), _p(offsets)),
+           "counts_offsets")
+    return counts, offsets
+
+
+def permutation(topk_idx, E, S=1, src_block=None):
+    """Step 3: the stable permutation and its inverse."""
+    topk_idx = _c(topk_idx, np.int32)
+    src_block = _c(src_block, np.int32)
+    M, k = topk_idx.shape
+    s2f = np.empty(M * k, np.int32)
+    f2s = np.empty(M * k, np.int32)
+    _check(_load().orc_permutation(M, E, k, S, _p(topk_idx), _p(src_block), _p(s2f), _p(f2s)), "permutation")
+    return s2f, f2s
+
+
+def dispatch(x, k, sorted_to_flat):
+    """Step 4: X_perm rows, a byte copy of the token rows."""
+    x = np.ascontiguousarray(x)
+    M, H = x.shape
+    s2f = _c(sorted_to_flat, np.int32)
+    xp = np.empty((M * k, H), x.dtype)
+    _check(_load().orc_dispatch(M, H, k, x.dtype.itemsize, _p(x), _p(s2f), _p(xp)), "dispatch")
+    return xp
+
+
+def ffn_rows(x, w_gate, w_up, w_down, k, S, sorted_to_flat, offsets, rows):
+    """Steps 5-6 for the listed sorted rows: (hact [n,F], y [n,H]) in float64."""
+    x = np.ascontiguousarray(x)
+    dt = _dtype_code(x)
+    E, F, H = w_gate.shape
+    wg, wu, wd = (np.ascontiguousarray(a, dtype=x.dtype) for a in (w_gate, w_up, w_down))
+    rows = _c(rows, np.int64)
+    n = rows.shape[0]
+    hact = np.empty((n, F), np.float64)
+    y = np.empty((n, H), np.float64)
+    _check(_load().orc_ffn_rows(H, F, E, S, k, dt, _p(x), _p(wg), _p(wu), _p(wd),
+                                _p(_c(sorted_to_flat, np.int32)), _p(_c(offsets, np.int32)), n, _p(rows),
+                                _p(hact), _p(y)), "ffn_rows")
+    return hact, y
+
+
+def combine_tokens(topk_w_sub, y_rows):
+    """Step 7: out[i] = sum_j w[i,j] * y_rows[i*k+j] in float64."""
+    w = _c(topk_w_sub, np.float32)
+    n, k = w.shape
+    y_rows = _c(y_rows, np.float64)
+    H = y_rows.shape[1]
+    out = np.empty((n, H), np.float64)
+    _check(_load().orc_combine_tokens(H, k, n, _p(w), _p(y_rows), _p(out)), "combine_tokens")
+    return out
+
+
+def moe_layer(x, logits, w_gate, w_up, w_down, k, S=1, src_block=None, tokens=None, want_rows=False):
+    """The whole layer.  Routing, counts, offsets and the permutation are
+    computed for every token; the FFN and the combine for ``tokens`` only
+    (all tokens if None).  Returns a dict of numpy arrays."""
+    x = np.ascontiguousarray(x)
+    dt = _dtype_code(x)
+    logits = _c(logits, np.float32)
+    M, H = x.shape
+    E, F, H2 = w_gate.shape
+    assert H2 == H and logits.shape == (M, E)
+    wg, wu, wd = (np.ascontiguousarray(a, dtype=x.dtype) for a in (w_gate, w_up, w_down))
+    src_block = _c(src_block, np.int32)
+    tok = None if tokens is None else _c(tokens, np.int64)
+    n_tok = M if tok is None else tok.shape[0]
+    r = dict(
+        topk_idx=np.empty((M, k), np.int32), topk_w=np.empty((M, k), np.float32),
+        counts=np.empty(S * E, np.int32), offsets=np.empty(S * E + 1, np.int32),
+        sorted_to_flat=np.empty(M * k, np.int32), flat_to_sorted=np.empty(M * k, np.int32),
+        out=np.empty((n_tok, H), np.float64))
+    hact = np.empty((n_tok * k, F), np.float64) if want_rows else None
+    y = np.empty((n_tok * k, H), np.float64) if want_rows else None
+    _check(_load().orc_moe_layer(M, H, F, E, k, S, dt, _p(x), _p(logits), _p(src_block), _p(wg), _p(wu), _p(wd),
+                                 n_tok, _p(tok), _p(r["topk_idx"]), _p(r["topk_w"]), _p(r["counts"]),
+                                 _p(r["offsets"]), _p(r["sorted_to_flat"]), _p(r["flat_to_sorted"]),
+                                 _p(r["out"]), _p(hact), _p(y)), "moe_layer")
+    if want_rows:
+        r["hact"] = hact
+        r["y"] = y
+    return r

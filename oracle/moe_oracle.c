@@ -1,0 +1,336 @@
+/*
+ * moe_oracle.c -- plain, slow CPU oracle for the MoE layer hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path links, loads or
+ * calls this file; only the test-suite, the smoke check and the benchmark's
+ * CPU-baseline leg do.  It shares no code, header, table or helper with the
+ * HIP library.
+ *
+ * What it computes (one MoE layer, the plain definition, in fp64):
+ *   route    -> per token the k largest gate logits, descending, ties to the
+ *               lower expert index; weights = softmax over the k chosen
+ *               logits.  ("topK weighted accumulation", PTO MoE article,
+ *               section on the seven serial stages; COMET review §4.1.1
+ *               names the Top-K reduction that couples rows along M.)
+ *   segments -> counts per (source block, expert) and their exclusive
+ *               prefix sum (PTO MoE article, "count-as-flag": the per-expert
+ *               row counts).
+ *   permute  -> pairs f = t*k + j listed segment by segment, increasing f
+ *               inside a segment (local reorder by expert, PTO MoE article,
+ *               seven serial stages; reorder by source first, COMET review
+ *               §4.1.2 "Layer0" rescheduling).
+ *   dispatch -> X_perm[r] = x[token of sorted_to_flat[r]] (COMET review §3.2,
+ *               Layer0 dispatch).
+ *   layer 0  -> g = X_r W_gate[e], u = X_r W_up[e], h = silu(g) * u (SwiGLU,
+ *               PTO MoE article "GMM1 -> SwiGLU"); for bf16 layers h is
+ *               rounded to bf16 (round to nearest even) because it is the
+ *               bf16 activation the down projection consumes.
+ *   layer 1  -> Y_r = h W_down[e], kept in fp64 (COMET review §3.2, Layer1).
+ *   combine  -> out[t] = sum_j w[t,j] * Y[flat_to_sorted[t*k+j]], summed from
+ *               zero in slot order j = 0..k-1 (COMET review §4.1.1 Top-K
+ *               reduction; PTO MoE article "Combine / Unpermute").
+ *
+ * Storage conventions (shared with the library's public header by
+ * specification only, not by code):
+ *   logits  [M,E] f32, x [M,H] (f32 or bf16 bits), src_block [M] i32 or NULL
+ *   W_gate, W_up stored [E,F,H] (row f of expert e holds column f of the
+ *   H x F matrix, i.e. the reduction index h is contiguous); W_down stored
+ *   [E,H,F] (row n holds column n of the F x H matrix).
+ *
+ * Every floating-point step runs in double from the exact input values
+ * (bf16 inputs are widened exactly).  Work over tokens / rows is spread over
+ * OpenMP threads; each output element is computed by exactly one thread in a
+ * fixed order, so results do not depend on the thread count.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_F32 0
+#define ORC_BF16 1
+
+#define ORC_OK 0
+#define ORC_EINVAL 1
+
+/* ---------------------------------------------------------------- bf16 --- */
+
+/* Exact widening of a bf16 bit pattern (the top 16 bits of an IEEE binary32). */
+double orc_bf16_bits_to_double(uint16_t b) {
+  uint32_t u = ((uint32_t)b) << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/*
+ * Round a double to the nearest bf16 value (8 significant bits, exponent
+ * range of binary32), ties to even.  Done directly from the double, so there
+ * is no double rounding through binary32.
+ */
+double orc_round_to_bf16(double x) {
+  if (x == 0.0 || isnan(x) || isinf(x)) return x;
+  int e;
+  double m = frexp(x, &e); /* x = m * 2^e, 0.5 <= |m| < 1 */
+  /* quantum of the bf16 grid at this binade: 2^(e-8); subnormal floor 2^-133 */
+  int q = e - 8;
+  if (q < -133) q = -133;
+  double scaled = ldexp(x, -q);          /* exact: only changes the exponent */
+  double r = nearbyint(scaled);          /* default rounding mode: ties-to-even */
+  double y = ldexp(r, q);
+  if (fabs(y) >= 0x1p128) y = copysign(INFINITY, x); /* beyond the largest finite bf16 */
+  (void)m;
+  return y;
+}
+
+/* Bits of the bf16 value equal to orc_round_to_bf16(x) (x already on the grid). */
+uint16_t orc_double_to_bf16_bits(double x) {
+  float f = (float)orc_round_to_bf16(x); /* exact: a bf16 value is a binary32 value */
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return (uint16_t)(u >> 16);
+}
+
+static double load_elem(const void* base, int dtype, int64_t i) {
+  if (dtype == ORC_F32) return (double)((const float*)base)[i];
+  return orc_bf16_bits_to_double(((const uint16_t*)base)[i]);
+}
+
+/* --------------------------------------------------------------- route --- */
+
+/*
+ * For each token t: the k experts with the largest logits, slot 0 the
+ * largest; equal logits go to the lower expert index (IEEE comparison, so
+ * -0.0 and +0.0 tie).  Selection k times over the experts not yet taken is
+ * the same as taking the first k of the sort by the key (-logit, e).
+ * Weights: softmax over the selected logits, shifted by the slot-0 logit.
+ */
+int orc_route(int64_t M, int E, int k, const float* logits, int32_t* topk_idx, float* topk_w) {
+  if (M < 0 || E < 1 || k < 1 || k > E) return ORC_EINVAL;
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < M; ++t) {
+    const float* row = logits + t * (int64_t)E;
+    char taken[1024];
+    int sel[1024];
+    memset(taken, 0, (size_t)E);
+    for (int j = 0; j < k; ++j) {
+      int best = -1;
+      for (int e = 0; e < E; ++e) {
+        if (taken[e]) continue;
+        if (best < 0 || row[e] > row[best]) best = e; /* strict: ties keep the lower index */
+      }
+      taken[best] = 1;
+      sel[j] = best;
+    }
+    double l0 = (double)row[sel[0]];
+    double denom = 0.0;
+    for (int j = 0; j < k; ++j) denom += exp((double)row[sel[j]] - l0);
+    for (int j = 0; j < k; ++j) {
+      topk_idx[t * k + j] = sel[j];
+      topk_w[t * k + j] = (float)(exp((double)row[sel[j]] - l0) / denom);
+    }
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------ segments --- */
+
+static int64_t seg_of(const int32_t* topk_idx, const int32_t* src_block, int E, int k, int64_t f) {
+  int64_t t = f / k;
+  int64_t s = src_block ? (int64_t)src_block[t] : 0;
+  return s * E + topk_idx[f];
+}
+
+/* counts[g] = number of pairs in segment g = src*E + expert; offsets = exclusive prefix sum. */
+int orc_counts_offsets(int64_t M, int E, int k, int S, const int32_t* topk_idx, const int32_t* src_block,
+                       int32_t* counts, int32_t* offsets) {
+  if (M < 0 || E < 1 || k < 1 || S < 1) return ORC_EINVAL;
+  int64_t G = (int64_t)S * E, R = M * k;
+  for (int64_t g = 0; g < G; ++g) counts[g] = 0;
+  for (int64_t f = 0; f < R; ++f) {
+    int64_t g = seg_of(topk_idx, src_block, E, k, f);
+    if (g < 0 || g >= G) return ORC_EINVAL;
+    counts[g] += 1;
+  }
+  offsets[0] = 0;
+  for (int64_t g = 0; g < G; ++g) offsets[g + 1] = offsets[g] + counts[g];
+  return ORC_OK;
+}
+
+/* Segment by segment, every pair of that segment in increasing flat index. */
+int orc_permutation(int64_t M, int E, int k, int S, const int32_t* topk_idx, const int32_t* src_block,
+                    int32_t* sorted_to_flat, int32_t* flat_to_sorted) {
+  if (M < 0 || E < 1 || k < 1 || S < 1) return ORC_EINVAL;
+  int64_t G = (int64_t)S * E, R = M * k, r = 0;
+  for (int64_t g = 0; g < G; ++g)
+    for (int64_t f = 0; f < R; ++f)
+      if (seg_of(topk_idx, src_block, E, k, f) == g) sorted_to_flat[r++] = (int32_t)f;
+  if (r != R) return ORC_EINVAL;
+  for (int64_t q = 0; q < R; ++q) flat_to_sorted[sorted_to_flat[q]] = (int32_t)q;
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------ dispatch --- */
+
+/* X_perm[r, :] = x[sorted_to_flat[r] / k, :], a byte copy of the token row. */
+int orc_dispatch(int64_t M, int H, int k, int elem_bytes, const void* x, const int32_t* sorted_to_flat,
+                 void* x_perm) {
+  if (M < 0 || H < 1 || k < 1 || (elem_bytes != 2 && elem_bytes != 4)) return ORC_EINVAL;
+  int64_t R = M * k;
+  size_t row = (size_t)H * (size_t)elem_bytes;
+  for (int64_t r = 0; r < R; ++r) {
+    int64_t t = sorted_to_flat[r] / k;
+    memcpy((char*)x_perm + (size_t)r * row, (const char*)x + (size_t)t * row, row);
+  }
+  return ORC_OK;
+}
+
+/* ----------------------------------------------------------- expert FFN --- */
+
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/*
+ * One routed row through expert e: Layer0 (gate and up products, SwiGLU,
+ * bf16 rounding of the activation for bf16 layers), then Layer1 (down).
+ * xrow is the token row widened to double.  hact [F] and y [H] in double.
+ */
+static void ffn_row(int H, int F, int dtype, const double* xrow, const void* w_gate, const void* w_up,
+                    const void* w_down, int e, double* hact, double* y) {
+  int64_t eHF = (int64_t)e * H * F;
+  for (int f = 0; f < F; ++f) {
+    double g = 0.0, u = 0.0;
+    int64_t wrow = eHF + (int64_t)f * H; /* W_gate / W_up stored [E,F,H] */
+    for (int h = 0; h < H; ++h) {
+      g += xrow[h] * load_elem(w_gate, dtype, wrow + h);
+      u += xrow[h] * load_elem(w_up, dtype, wrow + h);
+    }
+    double a = silu(g) * u;
+    hact[f] = (dtype == ORC_BF16) ? orc_round_to_bf16(a) : a;
+  }
+  for (int n = 0; n < H; ++n) {
+    double acc = 0.0;
+    int64_t wrow = eHF + (int64_t)n * F; /* W_down stored [E,H,F] */
+    for (int f = 0; f < F; ++f) acc += hact[f] * load_elem(w_down, dtype, wrow + f);
+    y[n] = acc;
+  }
+}
+
+/* Segment g containing sorted row r: offsets[g] <= r < offsets[g+1]. */
+static int64_t segment_of_row(const int32_t* offsets, int64_t G, int64_t r) {
+  for (int64_t g = 0; g < G; ++g)
+    if (offsets[g] <= r && r < offsets[g + 1]) return g;
+  return -1;
+}
+
+/*
+ * Layer0 + Layer1 for a list of sorted rows.  Row r belongs to segment g and
+ * uses expert g % E; its input is X_perm[r] = x[sorted_to_flat[r] / k].
+ * hact_out [n_rows, F] and y_out [n_rows, H] in double (either may be NULL).
+ */
+int orc_ffn_rows(int H, int F, int E, int S, int k, int dtype, const void* x, const void* w_gate,
+                 const void* w_up, const void* w_down, const int32_t* sorted_to_flat, const int32_t* offsets,
+                 int64_t n_rows, const int64_t* rows, double* hact_out, double* y_out) {
+  if (H < 1 || F < 1 || E < 1 || S < 1 || k < 1 || (dtype != ORC_F32 && dtype != ORC_BF16)) return ORC_EINVAL;
+  int64_t G = (int64_t)S * E;
+  int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+  for (int64_t i = 0; i < n_rows; ++i) {
+    int64_t r = rows[i];
+    int64_t g = segment_of_row(offsets, G, r);
+    if (g < 0) { bad = 1; continue; }
+    int e = (int)(g % E);
+    int64_t t = sorted_to_flat[r] / k;
+    double* xrow = (double*)malloc(sizeof(double) * (size_t)H);
+    double* hact = (double*)malloc(sizeof(double) * (size_t)F);
+    double* y = (double*)malloc(sizeof(double) * (size_t)H);
+    for (int h = 0; h < H; ++h) xrow[h] = load_elem(x, dtype, t * H + h);
+    ffn_row(H, F, dtype, xrow, w_gate, w_up, w_down, e, hact, y);
+    if (hact_out) memcpy(hact_out + i * F, hact, sizeof(double) * (size_t)F);
+    if (y_out) memcpy(y_out + i * H, y, sizeof(double) * (size_t)H);
+    free(xrow); free(hact); free(y);
+  }
+  return bad ? ORC_EINVAL : ORC_OK;
+}
+
+/* -------------------------------------------------------------- combine --- */
+
+/*
+ * out[i, :] = sum_{j=0..k-1} w[t,j] * Y[flat_to_sorted[t*k+j], :] for the
+ * listed tokens t = tokens[i]; y_rows supplies Y for the pairs of those
+ * tokens, in (i, j) order: y_rows[(i*k + j), :] is the row of pair t*k+j.
+ */
+int orc_combine_tokens(int H, int k, int64_t n_tok, const float* topk_w_sub, const double* y_rows, double* out) {
+  if (H < 1 || k < 1) return ORC_EINVAL;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n_tok; ++i) {
+    for (int n = 0; n < H; ++n) {
+      double acc = 0.0;
+      for (int j = 0; j < k; ++j) acc += (double)topk_w_sub[i * k + j] * y_rows[(i * k + j) * H + n];
+      out[i * H + n] = acc;
+    }
+  }
+  return ORC_OK;
+}
+
+/* ---------------------------------------------------------- whole layer --- */
+
+/*
+ * The whole layer, in the pages' order: route, segments, permutation over
+ * all tokens (always in full), then Layer0/Layer1 and the combine for the
+ * listed tokens only (all tokens when tokens == NULL; n_tok must then be M).
+ *
+ * Outputs: topk_idx/topk_w [M,k], counts [S*E], offsets [S*E+1],
+ * sorted_to_flat / flat_to_sorted [M*k] (all full); out [n_tok,H] double;
+ * hact [n_tok*k, F] and y [n_tok*k, H] double (may be NULL), row i*k+j
+ * belongs to pair (tokens[i], j).
+ */
+int orc_moe_layer(int64_t M, int H, int F, int E, int k, int S, int dtype, const void* x, const float* logits,
+                  const int32_t* src_block, const void* w_gate, const void* w_up, const void* w_down,
+                  int64_t n_tok, const int64_t* tokens, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                  int32_t* offsets, int32_t* sorted_to_flat, int32_t* flat_to_sorted, double* out, double* hact,
+                  double* y) {
+  int rc = orc_route(M, E, k, logits, topk_idx, topk_w);
+  if (rc) return rc;
+  rc = orc_counts_offsets(M, E, k, S, topk_idx, src_block, counts, offsets);
+  if (rc) return rc;
+  rc = orc_permutation(M, E, k, S, topk_idx, src_block, sorted_to_flat, flat_to_sorted);
+  if (rc) return rc;
+  if (!tokens && n_tok != M) return ORC_EINVAL;
+
+  int64_t n_pairs = n_tok * k;
+  int64_t* rows = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n_pairs > 0 ? n_pairs : 1));
+  float* wsub = (float*)malloc(sizeof(float) * (size_t)(n_pairs > 0 ? n_pairs : 1));
+  double* yrows = y ? y : (double*)malloc(sizeof(double) * (size_t)(n_pairs > 0 ? n_pairs : 1) * (size_t)H);
+  for (int64_t i = 0; i < n_tok; ++i) {
+    int64_t t = tokens ? tokens[i] : i;
+    if (t < 0 || t >= M) { rc = ORC_EINVAL; break; }
+    for (int j = 0; j < k; ++j) {
+      rows[i * k + j] = flat_to_sorted[t * k + j];
+      wsub[i * k + j] = topk_w[t * k + j];
+    }
+  }
+  if (!rc)
+    rc = orc_ffn_rows(H, F, E, S, k, dtype, x, w_gate, w_up, w_down, sorted_to_flat, offsets, n_pairs, rows, hact,
+                      yrows);
+  if (!rc) rc = orc_combine_tokens(H, k, n_tok, wsub, yrows, out);
+  free(rows);
+  free(wsub);
+  if (!y) free(yrows);
+  return rc;
+}
+
+/* Number of threads the parallel loops above use (for reporting). */
+int orc_num_threads(void) {
+  int n = 1;
+#pragma omp parallel
+  {
+#pragma omp single
+    {
+#ifdef _OPENMP
+      extern int omp_get_num_threads(void);
+      n = omp_get_num_threads();
+#endif
+    }
+  }
+  return n;
+}

@@ -1,0 +1,272 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+Each test checks the oracle against a brute-force or closed-form construction
+that does not share its code path: a Python sort for the routing, a numpy
+stable ordering for the permutation, a dense evaluation of every expert on
+every token for the layer, torch's bf16 conversion for the rounding, and
+exact algebraic identities (scaling, zero input, token permutation, expert
+relabelling).  A plausible slip in the oracle -- a dropped term, a flipped
+tie rule, a transposed weight, a wrong index into the permutation -- breaks
+at least one of these.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import moe_synth
+import oracle
+
+pytestmark = pytest.mark.filterwarnings("ignore::DeprecationWarning")
+
+
+# ----------------------------------------------------------------- helpers --
+
+def brute_topk(row, k):
+    order = sorted(range(len(row)), key=lambda e: (-float(row[e]), e))
+    return order[:k]
+
+
+def small_inputs(M, H, F, E, k, dtype, seed, S=1):
+    cfg = moe_synth.Config("pin", M, H, F, E, k, S, dtype, seed, 0.0, (M // S) if S > 1 else 0)
+    d = moe_synth.make_inputs(cfg)
+    return cfg, d
+
+
+def widen(a):
+    return moe_synth.bf16_bits_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
+def dense_layer(x, logits, wg, wu, wd, k, bf16):
+    """Every expert on every token, then the top-k mask and weights.
+
+    Independent of the oracle's routing / permutation / combine: experts are
+    chosen by argsort, weights by the full softmax renormalised over the
+    selected experts, and the FFN runs as dense numpy matmuls."""
+    X = widen(x)
+    L = logits.astype(np.float64)
+    M, E = L.shape
+    Wg, Wu, Wd = widen(wg), widen(wu), widen(wd)  # [E,F,H], [E,F,H], [E,H,F]
+    out = np.zeros((M, X.shape[1]))
+    # selection: stable argsort of -logit gives ties to the lower index
+    order = np.argsort(-L, axis=1, kind="stable")[:, :k]
+    p = np.exp(L - L.max(axis=1, keepdims=True))
+    p = p / p.sum(axis=1, keepdims=True)
+    for e in range(E):
+        G = X @ Wg[e].T
+        U = X @ Wu[e].T
+        Hh = G / (1.0 + np.exp(-G)) * U
+        if bf16:
+            Hh = np.vectorize(oracle.round_to_bf16)(Hh)
+        Y = Hh @ Wd[e].T
+        sel = (order == e)
+        mask = sel.any(axis=1)
+        w = np.where(mask, p[:, e] / np.take_along_axis(p, order, axis=1).sum(axis=1), 0.0)
+        # the combine consumes the stored f32 weights
+        w = w.astype(np.float32).astype(np.float64)
+        out += w[:, None] * Y
+    return out, order
+
+
+# -------------------------------------------------------------- bf16 pin --
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(0)
+    vals = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32),
+        (rng.standard_normal(2000) * 1e-30).astype(np.float32),
+        (rng.standard_normal(2000) * 1e30).astype(np.float32),
+    ])
+    # exact halfway cases: bf16 value + half a bf16 ulp (representable in f32)
+    base = moe_synth.bf16_bits_to_f32(rng.integers(0x0080, 0x7F00, size=2000, dtype=np.uint16))
+    half = (base.view(np.uint32) | np.uint32(0x8000)).view(np.float32)
+    vals = np.concatenate([vals, half, -half, np.float32([0.0, -0.0, 1.0, 1.00390625, 1.01171875])])
+    want = torch.from_numpy(vals).to(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([oracle.round_to_bf16(float(v)) for v in vals])
+    assert np.array_equal(got, want)
+
+
+# ------------------------------------------------------------- routing --
+
+@pytest.mark.parametrize("E,k", [(1, 1), (2, 1), (2, 2), (8, 2), (16, 8), (64, 4), (64, 64), (512, 16)])
+def test_route_matches_python_sort(E, k):
+    rng = np.random.default_rng(E * 100 + k)
+    M = 97
+    logits = rng.standard_normal((M, E)).astype(np.float32)
+    # plant ties: duplicated values, all-equal rows, signed zeros
+    logits[3, :] = 0.5
+    logits[5, : E // 2] = logits[5, E // 2 : 2 * (E // 2)]
+    logits[7, :] = -0.0
+    logits[7, ::2] = 0.0
+    logits[11] = np.round(logits[11] * 2) / 2
+    idx, w = oracle.route(logits, k)
+    for t in range(M):
+        assert list(idx[t]) == brute_topk(logits[t], k), t
+    assert list(idx[3]) == list(range(k))  # all-equal row: lowest indices in order
+    assert list(idx[7]) == list(range(k))  # +0.0 and -0.0 tie
+    assert np.all(np.abs(w.astype(np.float64).sum(axis=1) - 1.0) <= 4 * 2.0 ** -24 * k)
+
+
+def test_route_weights_closed_form_k2():
+    rng = np.random.default_rng(3)
+    logits = (rng.standard_normal((500, 8)) * 3).astype(np.float32)
+    idx, w = oracle.route(logits, 2)
+    l0 = np.take_along_axis(logits, idx[:, :1], 1)[:, 0].astype(np.float64)
+    l1 = np.take_along_axis(logits, idx[:, 1:2], 1)[:, 0].astype(np.float64)
+    w0 = 1.0 / (1.0 + np.exp(l1 - l0))
+    assert np.all(np.abs(w[:, 0] - w0) <= 2.0 ** -24)
+    assert np.all(np.abs(w[:, 1] - (1.0 - w0)) <= 2.0 ** -24)
+
+
+def test_route_weights_full_softmax_renormalised():
+    rng = np.random.default_rng(4)
+    logits = rng.standard_normal((300, 64)).astype(np.float32)
+    idx, w = oracle.route(logits, 4)
+    p = torch.softmax(torch.from_numpy(logits).double(), dim=1).numpy()
+    ps = np.take_along_axis(p, idx.astype(np.int64), 1)
+    want = ps / ps.sum(axis=1, keepdims=True)
+    assert np.max(np.abs(w - want)) <= 1e-7
+
+
+def test_route_k1_weight_is_exactly_one():
+    logits = np.random.default_rng(5).standard_normal((64, 16)).astype(np.float32)
+    idx, w = oracle.route(logits, 1)
+    assert np.all(w == 1.0)
+    assert np.array_equal(idx[:, 0], np.argmax(logits, axis=1))
+
+
+# ---------------------------------------------- counts / offsets / permute --
+
+@pytest.mark.parametrize("M,E,k,S", [(1, 1, 1, 1), (37, 8, 2, 1), (200, 64, 4, 1), (96, 16, 8, 8), (50, 4, 4, 2),
+                                     (0, 8, 2, 1)])
+def test_segments_and_permutation_brute_force(M, E, k, S):
+    rng = np.random.default_rng(M * 7 + E)
+    logits = rng.standard_normal((M, E)).astype(np.float32)
+    if M > 4:
+        logits[: M // 3, 0] += 10.0  # crowd expert 0, leave others light / empty
+    idx, _ = oracle.route(logits, k)
+    src = None if S == 1 else (np.arange(M) * S // max(M, 1)).astype(np.int32)
+    counts, offsets = oracle.counts_offsets(idx, E, S, src)
+    s2f, f2s = oracle.permutation(idx, E, S, src)
+    R = M * k
+    seg = [(0 if src is None else int(src[f // k])) * E + int(idx.reshape(-1)[f]) for f in range(R)]
+    # brute force: python stable sort of the flat indices by segment
+    want = sorted(range(R), key=lambda f: (seg[f], f))
+    assert list(s2f) == want
+    assert counts.sum() == R
+    assert np.array_equal(counts, np.bincount(np.array(seg, dtype=np.int64), minlength=S * E)[: S * E])
+    assert offsets[0] == 0 and offsets[-1] == R and np.all(np.diff(offsets) == counts)
+    assert sorted(s2f.tolist()) == list(range(R))  # bijection
+    assert np.array_equal(f2s[s2f], np.arange(R))
+    for g in range(S * E):  # stable inside every segment, and in the right segment
+        part = s2f[offsets[g]:offsets[g + 1]]
+        assert np.all(np.diff(part) > 0)
+        assert all(seg[f] == g for f in part)
+
+
+def test_dispatch_is_bitwise_row_copy():
+    cfg, d = small_inputs(40, 64, 64, 8, 2, "bf16", 11)
+    idx, _ = oracle.route(d["logits"], cfg.k)
+    s2f, _ = oracle.permutation(idx, cfg.E)
+    xp = oracle.dispatch(d["x"], cfg.k, s2f)
+    assert np.array_equal(xp, d["x"][s2f // cfg.k])
+
+
+# ------------------------------------------------------------------ layer --
+
+@pytest.mark.parametrize("dtype,E,k", [("f32", 4, 2), ("f32", 8, 8), ("bf16", 4, 2), ("bf16", 6, 3), ("f32", 1, 1)])
+def test_layer_matches_dense_brute_force(dtype, E, k):
+    cfg, d = small_inputs(48, 64, 96, E, k, dtype, 21 + E + k)
+    r = oracle.moe_layer(d["x"], d["logits"], d["w_gate"], d["w_up"], d["w_down"], k)
+    dense, order = dense_layer(d["x"], d["logits"], d["w_gate"], d["w_up"], d["w_down"], k, dtype == "bf16")
+    assert np.array_equal(r["topk_idx"], order)
+    np.testing.assert_allclose(r["out"], dense, rtol=1e-9, atol=1e-12)
+
+
+def test_layer_with_source_blocks_matches_dense():
+    cfg, d = small_inputs(64, 64, 64, 4, 2, "bf16", 33, S=4)
+    r = oracle.moe_layer(d["x"], d["logits"], d["w_gate"], d["w_up"], d["w_down"], 2, S=4, src_block=d["src_block"])
+    dense, _ = dense_layer(d["x"], d["logits"], d["w_gate"], d["w_up"], d["w_down"], 2, True)
+    np.testing.assert_allclose(r["out"], dense, rtol=1e-9, atol=1e-12)
+    assert r["counts"].sum() == 128 and r["offsets"][-1] == 128
+
+
+def test_top1_single_expert_is_one_dense_swiglu_ffn():
+    cfg, d = small_inputs(32, 64, 128, 1, 1, "f32", 41)
+    r = oracle.moe_layer(d["x"], d["logits"], d["w_gate"], d["w_up"], d["w_down"], 1)
+    assert np.all(r["topk_w"] == 1.0)
+    X = torch.from_numpy(d["x"]).double()
+    g = torch.matmul(X, torch.from_numpy(d["w_gate"][0]).double().T)
+    u = torch.matmul(X, torch.from_numpy(d["w_up"][0]).double().T)
+    y = torch.matmul(torch.nn.functional.silu(g) * u, torch.from_numpy(d["w_down"][0]).double().T)
+    np.testing.assert_allclose(r["out"], y.numpy(), rtol=1e-10, atol=1e-13)
+
+
+def test_token_subset_equals_full_layer_rows():
+    cfg, d = small_inputs(64, 64, 64, 8, 2, "bf16", 51)
+    full = oracle.moe_layer(d["x"], d["logits"], d["w_gate"], d["w_up"], d["w_down"], 2, want_rows=True)
+    toks = np.array([0, 5, 17, 63])
+    sub = oracle.moe_layer(d["x"], d["logits"], d["w_gate"], d["w_up"], d["w_down"], 2, tokens=toks, want_rows=True)
+    assert np.array_equal(sub["out"], full["out"][toks])
+    rows = (toks[:, None] * 2 + np.arange(2)).reshape(-1)
+    assert np.array_equal(sub["y"], full["y"][rows])
+
+
+# ----------------------------------------------------------- equivariances --
+
+def _layer(d, k, **kw):
+    return oracle.moe_layer(d["x"], d["logits"], d["w_gate"], d["w_up"], d["w_down"], k, **kw)["out"]
+
+
+def test_scaling_w_down_by_two_doubles_output_exactly():
+    cfg, d = small_inputs(32, 64, 64, 4, 2, "f32", 61)
+    base = _layer(d, 2)
+    d2 = dict(d, w_down=d["w_down"] * np.float32(2.0))
+    assert np.array_equal(_layer(d2, 2), 2.0 * base)
+
+
+def test_zero_input_gives_zero_output():
+    cfg, d = small_inputs(16, 64, 64, 4, 2, "bf16", 62)
+    d0 = dict(d, x=np.zeros_like(d["x"]))
+    assert np.all(_layer(d0, 2) == 0.0)
+
+
+def test_permuting_tokens_permutes_outputs():
+    cfg, d = small_inputs(40, 64, 64, 8, 2, "bf16", 63)
+    base = _layer(d, 2)
+    perm = np.random.default_rng(1).permutation(40)
+    dp = dict(d, x=d["x"][perm], logits=d["logits"][perm])
+    assert np.array_equal(_layer(dp, 2), base[perm])
+
+
+def test_relabelling_experts_leaves_output_unchanged():
+    cfg, d = small_inputs(40, 64, 64, 8, 2, "f32", 64)
+    base = _layer(d, 2)
+    perm = np.random.default_rng(2).permutation(8)
+    dp = dict(d, logits=d["logits"][:, perm], w_gate=d["w_gate"][perm], w_up=d["w_up"][perm],
+              w_down=d["w_down"][perm])
+    # N(0,1) f32 logits: ties have probability ~0, so the selected experts map one to one
+    assert np.array_equal(_layer(dp, 2), base)
+
+
+# ---------------------------------------------------------------- inputs --
+
+@pytest.mark.parametrize("name", ["mixtral", "phi35"])
+def test_stored_skew_scale_reproduces_target_std(name):
+    cfg = moe_synth.CONFIGS[name]
+    logits = moe_synth.make_logits(cfg)
+    idx, _ = oracle.route(logits, cfg.k)
+    counts, _ = oracle.counts_offsets(idx, cfg.E)
+    frac = counts / float(cfg.M * cfg.k)
+    assert abs(frac.std() - cfg.skew) <= 5e-4
+    if name == "phi35":
+        assert counts.min() < 500  # the lightest expert gets only a few hundred rows
+
+
+def test_unskewed_configs_are_near_uniform():
+    cfg = moe_synth.CONFIGS["qwen2"]
+    idx, _ = oracle.route(moe_synth.make_logits(cfg), cfg.k)
+    counts, _ = oracle.counts_offsets(idx, cfg.E)
+    frac = counts / float(cfg.R)
+    assert frac.std() < 0.25 / cfg.E

@@ -1,0 +1,188 @@
+"""Benchmark of the MoE layer hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config mixtral]
+
+A step is one pass of the whole layer over one batch of seeded synthetic
+input already resident in HBM: route -> dispatch (counts, offsets,
+permutation, gather) -> Layer0 grouped GEMM + SwiGLU -> Layer1 grouped GEMM ->
+top-k combine, issued through the library's C ABI (``--mode chain``, one
+launch per step with HIP events between them) or as one ``moe_layer`` call
+(``--mode layer``).  Prints ONE JSON line.
+
+`value` is the layer's algorithmic throughput, 6*R*H*F flop per step / step
+time, in TFLOP/s; the JSON also carries the layer time in microseconds, the
+grouped-GEMM TFLOP/s and its fraction of the bf16 matrix-core peak, the
+per-step times, a roofline object for the dominant kernel (Layer0 grouped
+GEMM) timed live with HIP events on the launch stream, and the CPU oracle
+timed on a bounded token sample on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+PEAK_F32_TFLOPS = 157.3     # MI355X f32 matrix peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="mixtral")
+    ap.add_argument("--mode", choices=("chain", "layer"), default="chain")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--n-mover", type=int, default=-1)
+    return ap.parse_args()
+
+
+def cpu_baseline(cfg, d, target_s):
+    """The oracle as it stands, on a seeded token sample sized for ~target_s."""
+    import moe_synth
+    import oracle
+    flop_tok = 6.0 * cfg.k * cfg.H * cfg.F
+    probe = moe_synth.token_sample(cfg, max(cfg.S, 2), seed_tag=11)
+    t0 = time.perf_counter()
+    oracle.moe_layer(d["x"], d["logits"], d["w_gate"], d["w_up"], d["w_down"], cfg.k, S=cfg.S,
+                     src_block=d["src_block"], tokens=probe)
+    dt_probe = time.perf_counter() - t0
+    n = int(max(cfg.S, min(cfg.M, round(len(probe) * target_s / max(dt_probe, 1e-3)))))
+    toks = moe_synth.token_sample(cfg, n, seed_tag=12)
+    t0 = time.perf_counter()
+    oracle.moe_layer(d["x"], d["logits"], d["w_gate"], d["w_up"], d["w_down"], cfg.k, S=cfg.S,
+                     src_block=d["src_block"], tokens=toks)
+    dt = time.perf_counter() - t0
+    flops = flop_tok * len(toks)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{len(toks)} of {cfg.M} tokens (all {cfg.k} routed rows each, seeded), full routing; "
+                      f"{dt:.1f} s fp64 on the host; per-token work is exactly linear, so the full layer "
+                      f"would take {dt * cfg.M / len(toks):.0f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1", "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    import combine_topk_gate_amd as moe
+    import moe_synth
+
+    def upload(arrs):
+        outd = {}
+        for key, a in arrs.items():
+            if a is None:
+                outd[key] = None
+            elif a.dtype == np.uint16:
+                outd[key] = torch.from_numpy(a.view(np.int16)).to("cuda:0").view(torch.bfloat16)
+            else:
+                outd[key] = torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+        return outd
+
+    moe.load_library()
+    cfg = moe_synth.config(args.config)
+    d = moe_synth.make_inputs(cfg)
+    g = upload(d)
+    dev = torch.device("cuda:0")
+    p = moe.problem(cfg.M, cfg.H, cfg.F, cfg.E, cfg.k, cfg.S, cfg.dtype)
+    M, k, H, F, G, R = cfg.M, cfg.k, cfg.H, cfg.F, cfg.S * cfg.E, cfg.R
+    act = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    idx = torch.empty((M, k), dtype=torch.int32, device=dev)
+    w = torch.empty((M, k), dtype=torch.float32, device=dev)
+    counts = torch.empty(G, dtype=torch.int32, device=dev)
+    offsets = torch.empty(G + 1, dtype=torch.int32, device=dev)
+    s2f = torch.empty(R, dtype=torch.int32, device=dev)
+    f2s = torch.empty(R, dtype=torch.int32, device=dev)
+    xp = torch.empty((R, H), dtype=act, device=dev)
+    hact = torch.empty((R, F), dtype=act, device=dev)
+    y = torch.empty((R, H), dtype=torch.float32, device=dev)
+    out = torch.empty((M, H), dtype=torch.float32, device=dev)
+    ws_d = torch.empty(max(4, moe.moe_workspace_bytes(p, moe.MOE_OP_DISPATCH)), dtype=torch.uint8, device=dev)
+    ws_l = torch.empty(moe.moe_workspace_bytes(p, moe.MOE_OP_LAYER), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    src = g.get("src_block")
+
+    nev = 6
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+
+    def step_chain(ev=None):
+        if ev: ev[0].record(stream)
+        moe.moe_route(p, g["logits"], idx, w, stream)
+        if ev: ev[1].record(stream)
+        moe.moe_dispatch(p, g["x"], idx, src, counts, offsets, s2f, f2s, xp, ws_d, stream)
+        if ev: ev[2].record(stream)
+        moe.moe_grouped_gemm(p, 0, xp, g["w_gate"], g["w_up"], offsets, hact, None, stream)
+        if ev: ev[3].record(stream)
+        moe.moe_grouped_gemm(p, 1, hact, g["w_down"], None, offsets, y, None, stream)
+        if ev: ev[4].record(stream)
+        moe.moe_combine(p, y, w, f2s, out, stream)
+        if ev: ev[5].record(stream)
+
+    def step_layer(ev=None):
+        if ev: ev[0].record(stream)
+        moe.moe_layer(p, g["x"], g["logits"], src, g["w_gate"], g["w_up"], g["w_down"], out, ws_l,
+                      n_mover=args.n_mover, stream=stream)
+        if ev: ev[5].record(stream)
+
+    step = step_chain if args.mode == "chain" else step_layer
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(events[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+
+    flops = 6.0 * R * H * F
+    res = {"metric": "MoE layer us + grouped-GEMM TFLOP/s (% MFMA peak), Mixtral shape M=8192",
+           "value": flops / (ms_step * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+           "data": "synthetic (seeded N(0,1) tokens and logits, N(0,0.02^2) weights, random-init)",
+           "config": {"workload": f"{cfg.name}: MoE layer M={M} H={H} F={F} E={cfg.E} topk={k} S={cfg.S}",
+                      "tokens": M, "hidden": H, "ffn": F, "experts": cfg.E, "topk": k, "src_blocks": cfg.S,
+                      "mode": args.mode},
+           "layer_us": ms_step * 1e3}
+    if args.mode == "chain":
+        per = np.array([[events[i][j].elapsed_time(events[i][j + 1]) for j in range(nev - 1)]
+                        for i in range(args.steps)]) * 1e3  # us
+        mean = per.mean(axis=0)
+        names = ["route", "dispatch", "gemm_l0", "gemm_l1", "combine"]
+        res["step_us"] = {n: float(v) for n, v in zip(names, mean)}
+        t_gemm = (mean[2] + mean[3]) * 1e-6
+        peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+        res["grouped_gemm_tflops"] = flops / t_gemm / 1e12
+        res["grouped_gemm_pct_peak"] = 100.0 * res["grouped_gemm_tflops"] / peak
+        disp_bytes = M * H * (2 if cfg.dtype == "bf16" else 4) * (1 + k) + R * 4
+        comb_bytes = R * H * 4 + M * H * 4 + M * k * 8
+        res["dispatch_gbs"] = disp_bytes / (mean[1] * 1e-6) / 1e9
+        res["combine_gbs"] = comb_bytes / (mean[4] * 1e-6) / 1e9
+        l0_flops = 4.0 * R * H * F
+        ach = l0_flops / (mean[2] * 1e-6) / 1e12
+        res["roofline"] = {"kernel": "grouped_gemm_bf16_kernel<0> (Layer0 gate/up + SwiGLU)", "bound": "mfma",
+                           "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak, "traffic": None,
+                           "launch_us": float(mean[2]), "algorithmic": f"4*R*H*F = {l0_flops:.4g} flop per launch"}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, d, args.cpu_seconds)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,316 @@
+// C ABI of the library: host-side argument checks, workspace carving and
+// kernel launches.  Every entry point only enqueues work on the caller's
+// stream; none synchronises (except moe_debug_device_status, a test hook).
+#include <string.h>
+
+#include "common.hpp"
+#include "launch.hpp"
+#include "layer.hpp"
+
+namespace {
+
+using namespace moe;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t elem_bytes(const moe_problem_t* p) { return p->dtype == MOE_DTYPE_BF16 ? 2 : 4; }
+
+moe_status_t check_problem(const moe_problem_t* p) {
+  if (!p) return MOE_ERR_INVALID_ARGUMENT;
+  const int64_t M = p->num_tokens;
+  if (M < 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (p->hidden < 64 || p->hidden > 65536 || p->hidden % 64) return MOE_ERR_INVALID_ARGUMENT;
+  if (p->ffn < 64 || p->ffn > 65536 || p->ffn % 64) return MOE_ERR_INVALID_ARGUMENT;
+  if (p->num_experts < 1 || p->num_experts > 512) return MOE_ERR_INVALID_ARGUMENT;
+  if (p->topk < 1 || p->topk > 16 || p->topk > p->num_experts) return MOE_ERR_INVALID_ARGUMENT;
+  if (p->num_src_blocks < 1 || (int64_t)p->num_src_blocks * p->num_experts > 1024) return MOE_ERR_INVALID_ARGUMENT;
+  if (p->dtype != MOE_DTYPE_F32 && p->dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARGUMENT;
+  const int64_t R = M * p->topk;
+  if (R >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
+  const int64_t wide = p->hidden > p->ffn ? p->hidden : p->ffn;
+  if (R * wide >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)p->num_experts * p->hidden * p->ffn >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Workspace of the whole layer, carved in this order (each region 256-B aligned).
+struct LayerWs {
+  size_t status, topk_idx, topk_w, counts, offsets, s2f, f2s, perm, x_perm, hact, y, fused, total;
+};
+
+LayerWs layer_ws(const moe_problem_t* p) {
+  const int64_t M = p->num_tokens, R = M * p->topk;
+  const int G = p->num_src_blocks * p->num_experts;
+  const size_t eb = elem_bytes(p);
+  const PermutePlan pl = permute_plan(M, p->topk, G);
+  LayerWs w;
+  size_t o = 0;
+  w.status = o; o += align_up(kAlign);
+  w.topk_idx = o; o += align_up((size_t)R * 4);
+  w.topk_w = o; o += align_up((size_t)R * 4);
+  w.counts = o; o += align_up((size_t)G * 4);
+  w.offsets = o; o += align_up((size_t)(G + 1) * 4);
+  w.s2f = o; o += align_up((size_t)R * 4);
+  w.f2s = o; o += align_up((size_t)R * 4);
+  w.perm = o; o += align_up(permute_ws_bytes(pl));
+  w.x_perm = o; o += align_up((size_t)R * p->hidden * eb);
+  w.hact = o; o += align_up((size_t)R * p->ffn * eb);
+  w.y = o; o += align_up((size_t)R * p->hidden * 4);
+  w.fused = o; o += align_up(fused_ws_bytes(p->num_tokens, p->hidden, p->ffn, p->num_experts, p->topk,
+                                             p->num_src_blocks));
+  w.total = o;
+  return w;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(ws) + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return (1 << 16) | 0; }
+
+const char* moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    case MOE_ERR_DEVICE_TIMEOUT: return "MOE_ERR_DEVICE_TIMEOUT";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+size_t moe_workspace_bytes(const moe_problem_t* p, int32_t op) {
+  if (check_problem(p) != MOE_OK) return 0;
+  const int G = p->num_src_blocks * p->num_experts;
+  switch (op) {
+    case MOE_OP_DISPATCH: return permute_ws_bytes(permute_plan(p->num_tokens, p->topk, G));
+    case MOE_OP_GROUPED_GEMM: return 0;
+    case MOE_OP_LAYER: return layer_ws(p).total;
+  }
+  return 0;
+}
+
+moe_status_t moe_route(const moe_problem_t* p, const float* logits, int32_t* topk_idx, float* topk_w, void* stream) {
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (p->num_tokens == 0) return MOE_OK;
+  if (!logits || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4)) return MOE_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_route(logits, p->num_tokens, p->num_experts, p->topk, topk_idx, topk_w,
+                                 (hipStream_t)stream));
+}
+
+moe_status_t moe_dispatch(const moe_problem_t* p, const void* x, const int32_t* topk_idx, const int32_t* src_block,
+                          int32_t* counts, int32_t* offsets, int32_t* sorted_to_flat, int32_t* flat_to_sorted,
+                          void* x_perm, void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!counts || !offsets) return MOE_ERR_INVALID_ARGUMENT;
+  if (p->num_src_blocks > 1 && !src_block && p->num_tokens > 0) return MOE_ERR_INVALID_ARGUMENT;
+  const int64_t M = p->num_tokens;
+  if (M > 0) {
+    if (!x || !topk_idx || !sorted_to_flat || !flat_to_sorted || !x_perm) return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned(x, 16) || !aligned(x_perm, 16)) return MOE_ERR_INVALID_ARGUMENT;
+  }
+  const int G = p->num_src_blocks * p->num_experts;
+  const PermutePlan pl = permute_plan(M, p->topk, G);
+  if (ws_bytes < permute_ws_bytes(pl) || !ws) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_permute(pl, topk_idx, p->num_src_blocks > 1 ? src_block : nullptr, p->num_experts, p->topk,
+                                counts, offsets, sorted_to_flat, flat_to_sorted, (int32_t*)ws, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = launch_dispatch_copy(x, M, (int64_t)p->hidden * elem_bytes(p), p->topk, flat_to_sorted, x_perm, s);
+  return hip_status(e);
+}
+
+moe_status_t moe_grouped_gemm(const moe_problem_t* p, int32_t layer, const void* a, const void* w0, const void* w1,
+                              const int32_t* offsets, void* c, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (layer != 0 && layer != 1) return MOE_ERR_INVALID_ARGUMENT;
+  if (!offsets || !w0 || (layer == 0 && !w1)) return MOE_ERR_INVALID_ARGUMENT;
+  const int64_t R = p->num_tokens * p->topk;
+  if (R > 0 && (!a || !c)) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(a, 16) || !aligned(c, 16) || !aligned(w0, 16) || (layer == 0 && !aligned(w1, 16)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  GemmProblem gp;
+  gp.layer = layer;
+  gp.a = a;
+  gp.w0 = w0;
+  gp.w1 = layer == 0 ? w1 : nullptr;
+  gp.offsets = offsets;
+  gp.c = c;
+  gp.R = R;
+  gp.K = layer == 0 ? p->hidden : p->ffn;
+  gp.N = layer == 0 ? p->ffn : p->hidden;
+  gp.E = p->num_experts;
+  gp.G = p->num_src_blocks * p->num_experts;
+  hipStream_t s = (hipStream_t)stream;
+  return hip_status(p->dtype == MOE_DTYPE_BF16 ? launch_grouped_gemm_bf16(gp, s) : launch_grouped_gemm_f32(gp, s));
+}
+
+moe_status_t moe_combine(const moe_problem_t* p, const float* y, const float* topk_w, const int32_t* flat_to_sorted,
+                         float* out, void* stream) {
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (p->num_tokens == 0) return MOE_OK;
+  if (!y || !topk_w || !flat_to_sorted || !out) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(y, 16) || !aligned(out, 16) || !aligned(topk_w, 4)) return MOE_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_combine(y, topk_w, flat_to_sorted, p->num_tokens, p->hidden, p->topk, out,
+                                   (hipStream_t)stream));
+}
+
+int32_t moe_layer_default_movers(const moe_problem_t* p) {
+  if (check_problem(p) != MOE_OK) return -1;
+  return fused_default_movers(p->num_tokens, p->hidden, p->ffn, p->num_experts, p->topk, p->num_src_blocks,
+                              p->dtype, device_cu_count());
+}
+
+moe_status_t moe_layer(const moe_problem_t* p, const void* x, const float* logits, const int32_t* src_block,
+                       const void* w_gate, const void* w_up, const void* w_down, float* out,
+                       const moe_layer_aux_t* aux, const moe_layer_opts_t* opts, void* ws, size_t ws_bytes,
+                       void* stream) {
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  const int64_t M = p->num_tokens;
+  if (!w_gate || !w_up || !w_down) return MOE_ERR_INVALID_ARGUMENT;
+  if (M > 0 && (!x || !logits || !out)) return MOE_ERR_INVALID_ARGUMENT;
+  if (p->num_src_blocks > 1 && !src_block && M > 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(w_down, 16))
+    return MOE_ERR_INVALID_ARGUMENT;
+  const LayerWs L = layer_ws(p);
+  if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned(ws, kAlign)) return MOE_ERR_INVALID_ARGUMENT;
+  moe_layer_aux_t a;
+  memset(&a, 0, sizeof a);
+  if (aux) a = *aux;
+  if (a.x_perm && !aligned(a.x_perm, 16)) return MOE_ERR_INVALID_ARGUMENT;
+  if (a.hact && !aligned(a.hact, 16)) return MOE_ERR_INVALID_ARGUMENT;
+  if (a.y && !aligned(a.y, 16)) return MOE_ERR_INVALID_ARGUMENT;
+  const int G = p->num_src_blocks * p->num_experts;
+  int32_t* idx = a.topk_idx ? a.topk_idx : at<int32_t>(ws, L.topk_idx);
+  float* w = a.topk_w ? a.topk_w : at<float>(ws, L.topk_w);
+  int32_t* counts = a.counts ? a.counts : at<int32_t>(ws, L.counts);
+  int32_t* offsets = a.offsets ? a.offsets : at<int32_t>(ws, L.offsets);
+  int32_t* s2f = a.sorted_to_flat ? a.sorted_to_flat : at<int32_t>(ws, L.s2f);
+  int32_t* f2s = a.flat_to_sorted ? a.flat_to_sorted : at<int32_t>(ws, L.f2s);
+  void* xp = a.x_perm ? a.x_perm : at<void>(ws, L.x_perm);
+  void* hact = a.hact ? a.hact : at<void>(ws, L.hact);
+  float* y = a.y ? a.y : at<float>(ws, L.y);
+  int32_t* status = at<int32_t>(ws, L.status);
+  const int32_t* src = p->num_src_blocks > 1 ? src_block : nullptr;
+  hipStream_t s = (hipStream_t)stream;
+
+  moe_layer_opts_t o;
+  o.n_mover = -1;
+  o.grid = 0;
+  o.fused = 1;
+  o.spin_limit = 0;
+  if (opts) o = *opts;
+
+  // cleared with a fill kernel rather than a memset node, so that the call
+  // can be captured into a HIP graph
+  hipError_t e = launch_fill_i32(status, 1, 0, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  if (M == 0) {
+    // nothing routed: counts and offsets are all zero
+    e = launch_fill_i32(counts, G, 0, s);
+    if (e == hipSuccess) e = launch_fill_i32(offsets, G + 1, 0, s);
+    return hip_status(e);
+  }
+  e = launch_route(logits, M, p->num_experts, p->topk, idx, w, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  const PermutePlan pl = permute_plan(M, p->topk, G);
+  e = launch_permute(pl, idx, src, p->num_experts, p->topk, counts, offsets, s2f, f2s, at<int32_t>(ws, L.perm), s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+
+  const int cus = device_cu_count();
+  const int movers = o.n_mover >= 0 ? o.n_mover
+                                    : fused_default_movers(M, p->hidden, p->ffn, p->num_experts, p->topk,
+                                                           p->num_src_blocks, p->dtype, cus);
+  const bool fused = o.fused != 0 && p->dtype == MOE_DTYPE_BF16 && movers > 0;
+  if (fused) {
+    FusedArgs fa;
+    fa.M = M;
+    fa.H = p->hidden;
+    fa.F = p->ffn;
+    fa.E = p->num_experts;
+    fa.k = p->topk;
+    fa.G = G;
+    fa.x = x;
+    fa.w_gate = w_gate;
+    fa.w_up = w_up;
+    fa.w_down = w_down;
+    fa.topk_w = w;
+    fa.offsets = offsets;
+    fa.s2f = s2f;
+    fa.f2s = f2s;
+    fa.x_perm = xp;
+    fa.hact = hact;
+    fa.y = y;
+    fa.out = out;
+    fa.status = status;
+    fa.flags = at<int32_t>(ws, L.fused);
+    fa.grid = o.grid > 0 ? o.grid : cus;
+    fa.n_mover = movers;
+    fa.spin_limit = o.spin_limit;
+    moe_status_t fs = fused_check(fa, cus);
+    if (fs != MOE_OK) return fs;
+    return hip_status(launch_fused_layer(fa, s));
+  }
+  e = launch_dispatch_copy(x, M, (int64_t)p->hidden * elem_bytes(p), p->topk, f2s, xp, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  GemmProblem gp;
+  gp.R = M * p->topk;
+  gp.E = p->num_experts;
+  gp.G = G;
+  gp.offsets = offsets;
+  gp.layer = 0;
+  gp.a = xp;
+  gp.w0 = w_gate;
+  gp.w1 = w_up;
+  gp.c = hact;
+  gp.K = p->hidden;
+  gp.N = p->ffn;
+  e = p->dtype == MOE_DTYPE_BF16 ? launch_grouped_gemm_bf16(gp, s) : launch_grouped_gemm_f32(gp, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  gp.layer = 1;
+  gp.a = hact;
+  gp.w0 = w_down;
+  gp.w1 = nullptr;
+  gp.c = y;
+  gp.K = p->ffn;
+  gp.N = p->hidden;
+  e = p->dtype == MOE_DTYPE_BF16 ? launch_grouped_gemm_bf16(gp, s) : launch_grouped_gemm_f32(gp, s);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(launch_combine(y, w, f2s, M, p->hidden, p->topk, out, s));
+}
+
+moe_status_t moe_debug_device_status(const moe_problem_t* p, void* ws, size_t ws_bytes, void* stream) {
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  const LayerWs L = layer_ws(p);
+  if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  int32_t v = 0;
+  hipStream_t s = (hipStream_t)stream;
+  if (hipMemcpyAsync(&v, at<int32_t>(ws, L.status), sizeof v, hipMemcpyDeviceToHost, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return MOE_ERR_HIP;
+  return v == 0 ? MOE_OK : (moe_status_t)v;
+}
+
+}  // extern "C"

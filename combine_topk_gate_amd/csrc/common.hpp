@@ -1,0 +1,54 @@
+// Internal helpers shared by the library's HIP kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// Device-side status words kept at the start of the fused layer's workspace.
+constexpr int kStatusOk = 0;
+constexpr int kStatusTimeout = 5;
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int lane = __lane_id();
+  return (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+}
+
+// f32 -> bf16, round to nearest even (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
+
+// Top-k weighted reduction of one 4-wide column group, shared by the
+// stand-alone combine and the fused layer so both give identical bits.
+__device__ __forceinline__ float4 combine_group(const float* __restrict__ y, const float* __restrict__ w,
+                                                const int32_t* __restrict__ rows, int k, int64_t H, int64_t n) {
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < k; ++j) {
+    const float wj = w[j];
+    const float4 v = *reinterpret_cast<const float4*>(y + (int64_t)rows[j] * H + n);
+    acc.x = fmaf(wj, v.x, acc.x);
+    acc.y = fmaf(wj, v.y, acc.y);
+    acc.z = fmaf(wj, v.z, acc.z);
+    acc.w = fmaf(wj, v.w, acc.w);
+  }
+  return acc;
+}
+
+inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+}  // namespace moe

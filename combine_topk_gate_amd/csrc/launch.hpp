@@ -1,0 +1,51 @@
+// Host-side launchers of the library's kernels (internal; the public entry
+// points in api.hip validate arguments and call these).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_route(const float* logits, int64_t M, int E, int k, int32_t* topk_idx, float* topk_w,
+                        hipStream_t s);
+
+// Segment bookkeeping: per-chunk histograms, scan, stable ranks.
+struct PermutePlan {
+  int64_t R;
+  int G;
+  int chunk;   // pairs per block
+  int blocks;  // ceil(R / chunk)
+};
+PermutePlan permute_plan(int64_t M, int k, int G);
+size_t permute_ws_bytes(const PermutePlan& pl);
+hipError_t launch_permute(const PermutePlan& pl, const int32_t* topk_idx, const int32_t* src_block, int E, int k,
+                          int32_t* counts, int32_t* offsets, int32_t* sorted_to_flat, int32_t* flat_to_sorted,
+                          int32_t* ws, hipStream_t s);
+hipError_t launch_dispatch_copy(const void* x, int64_t M, int64_t row_bytes, int k, const int32_t* flat_to_sorted,
+                                void* x_perm, hipStream_t s);
+
+// Grouped GEMM (layer 0: gate/up + SwiGLU; layer 1: down).
+struct GemmProblem {
+  int layer;
+  const void* a;
+  const void* w0;
+  const void* w1;
+  const int32_t* offsets;
+  void* c;
+  int64_t R;
+  int K;  // reduction length: H (layer 0) or F (layer 1)
+  int N;  // output columns: F (layer 0) or H (layer 1)
+  int E;
+  int G;
+};
+hipError_t launch_grouped_gemm_bf16(const GemmProblem& gp, hipStream_t s);
+hipError_t launch_grouped_gemm_f32(const GemmProblem& gp, hipStream_t s);
+
+hipError_t launch_combine(const float* y, const float* topk_w, const int32_t* flat_to_sorted, int64_t M, int H,
+                          int k, float* out, hipStream_t s);
+
+int device_cu_count();
+
+}  // namespace moe

@@ -1,0 +1,42 @@
+// Fused MoE layer (internal interface).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+typedef const int32_t* src_ptr_t;
+
+struct FusedArgs {
+  int64_t M;
+  int H, F, E, k, G;
+  const void* x;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  const float* topk_w;
+  const int32_t* offsets;
+  const int32_t* s2f;
+  const int32_t* f2s;
+  void* x_perm;
+  void* hact;
+  float* y;
+  float* out;
+  int32_t* status;
+  int32_t* flags;
+  int grid;
+  int n_mover;
+  int spin_limit;
+};
+
+size_t fused_ws_bytes(int64_t M, int H, int F, int E, int k, int S);
+int fused_default_movers(int64_t M, int H, int F, int E, int k, int S, int dtype, int cus);
+moe_status_t fused_check(const FusedArgs& a, int cus);
+hipError_t launch_fused_layer(const FusedArgs& a, hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,198 @@
+// Counts, offsets, stable permutation and the dispatch copy.
+//
+// PTO MoE article (seven serial stages: local reorder by expert; the
+// count-as-flag paragraph: per-expert row counts) and COMET paper review
+// §4.1.2 (Layer0: order tokens by source first).  Pair f = t*k + j goes to
+// segment g = src_block[t] * E + topk_idx[t, j]; the sorted order lists the
+// segments in turn and, inside a segment, the pairs by increasing f.
+//
+// No atomic operation decides an order, so every output is bit-exact and
+// independent of scheduling:
+//   seg_count  one block per chunk of pairs: LDS histogram over the G
+//              segments (atomics only add counts, which commute).
+//   seg_scan   one block: per segment, exclusive prefix over the chunks;
+//              counts; exclusive prefix over segments = offsets; the
+//              start of every (chunk, segment) run.
+//   seg_rank   one block per chunk, walking it 256 pairs at a time in flat
+//              order: inside a wave, lanes with equal keys find each other
+//              with one ballot per key bit, and the rank among them is a
+//              popcount of the lower lanes; waves are ordered through a small
+//              per-wave count table in LDS.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+constexpr int kPermThreads = 256;
+constexpr int kPermWaves = kPermThreads / kWave;
+constexpr int kMaxSegments = 1024;
+
+__device__ __forceinline__ int seg_of(const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ src_block,
+                                      int E, int k, int64_t f) {
+  const int s = src_block ? src_block[f / k] : 0;
+  return s * E + topk_idx[f];
+}
+
+__global__ __launch_bounds__(kPermThreads) void seg_count_kernel(const int32_t* __restrict__ topk_idx,
+                                                                 const int32_t* __restrict__ src_block, int E, int k,
+                                                                 int64_t R, int G, int chunk,
+                                                                 int32_t* __restrict__ block_hist) {
+  __shared__ int hist[kMaxSegments];
+  for (int g = threadIdx.x; g < G; g += kPermThreads) hist[g] = 0;
+  __syncthreads();
+  const int64_t begin = (int64_t)blockIdx.x * chunk;
+  const int64_t end = (begin + chunk < R) ? begin + chunk : R;
+  for (int64_t f = begin + threadIdx.x; f < end; f += kPermThreads)
+    atomicAdd(&hist[seg_of(topk_idx, src_block, E, k, f)], 1);
+  __syncthreads();
+  for (int g = threadIdx.x; g < G; g += kPermThreads) block_hist[(int64_t)blockIdx.x * G + g] = hist[g];
+}
+
+__global__ __launch_bounds__(kMaxSegments) void seg_scan_kernel(int G, int blocks, int64_t R,
+                                                                int32_t* __restrict__ block_hist,
+                                                                int32_t* __restrict__ counts,
+                                                                int32_t* __restrict__ offsets) {
+  __shared__ int s[kMaxSegments];
+  const int g = threadIdx.x;
+  int total = 0;
+  if (g < G) {
+    for (int b = 0; b < blocks; ++b) {
+      const int c = block_hist[(int64_t)b * G + g];
+      block_hist[(int64_t)b * G + g] = total;
+      total += c;
+    }
+    counts[g] = total;
+  }
+  s[g] = (g < G) ? total : 0;
+  __syncthreads();
+  for (int off = 1; off < kMaxSegments; off <<= 1) {
+    const int v = (g >= off) ? s[g - off] : 0;
+    __syncthreads();
+    s[g] += v;
+    __syncthreads();
+  }
+  if (g < G) {
+    const int start = s[g] - total;  // exclusive prefix
+    offsets[g] = start;
+    for (int b = 0; b < blocks; ++b) block_hist[(int64_t)b * G + g] += start;
+  }
+  if (g == 0) offsets[G] = (int)R;
+}
+
+__global__ __launch_bounds__(kPermThreads) void seg_rank_kernel(const int32_t* __restrict__ topk_idx,
+                                                                const int32_t* __restrict__ src_block, int E, int k,
+                                                                int64_t R, int G, int chunk, int nbits,
+                                                                const int32_t* __restrict__ block_base,
+                                                                int32_t* __restrict__ sorted_to_flat,
+                                                                int32_t* __restrict__ flat_to_sorted) {
+  __shared__ int running[kMaxSegments];
+  __shared__ int wcnt[kPermWaves][kMaxSegments];
+  const int tid = threadIdx.x, w = tid / kWave;
+  for (int g = tid; g < G; g += kPermThreads) {
+    running[g] = block_base[(int64_t)blockIdx.x * G + g];
+#pragma unroll
+    for (int q = 0; q < kPermWaves; ++q) wcnt[q][g] = 0;
+  }
+  __syncthreads();
+  const int64_t begin = (int64_t)blockIdx.x * chunk;
+  const int64_t end = (begin + chunk < R) ? begin + chunk : R;
+  const uint64_t below = lanemask_lt();
+  for (int64_t base = begin; base < end; base += kPermThreads) {
+    const int64_t f = base + tid;
+    const bool valid = f < end;
+    const int g = valid ? seg_of(topk_idx, src_block, E, k, f) : 0;
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const int bit = (g >> b) & 1;
+      const uint64_t ones = __ballot(valid && bit);
+      peers &= bit ? ones : ~ones;
+    }
+    const int rank = __popcll(peers & below);
+    const int group = __popcll(peers);
+    if (valid && rank == 0) wcnt[w][g] = group;
+    __syncthreads();
+    if (valid) {
+      int pos = running[g] + rank;
+      for (int q = 0; q < w; ++q) pos += wcnt[q][g];
+      sorted_to_flat[pos] = (int32_t)f;
+      flat_to_sorted[f] = pos;
+    }
+    __syncthreads();
+    if (valid && rank == 0) {
+      atomicAdd(&running[g], group);
+      wcnt[w][g] = 0;
+    }
+    __syncthreads();
+  }
+}
+
+PermutePlan permute_plan(int64_t M, int k, int G) {
+  PermutePlan pl;
+  pl.R = M * k;
+  pl.G = G;
+  int64_t chunk = 4096;
+  const int64_t want = (pl.R + 1023) / 1024;  // at most 1024 chunks
+  if (want > chunk) chunk = ((want + kPermThreads - 1) / kPermThreads) * kPermThreads;
+  pl.chunk = (int)chunk;
+  pl.blocks = (int)((pl.R + chunk - 1) / chunk);
+  return pl;
+}
+
+size_t permute_ws_bytes(const PermutePlan& pl) { return (size_t)(pl.blocks > 0 ? pl.blocks : 1) * pl.G * 4; }
+
+hipError_t launch_permute(const PermutePlan& pl, const int32_t* topk_idx, const int32_t* src_block, int E, int k,
+                          int32_t* counts, int32_t* offsets, int32_t* sorted_to_flat, int32_t* flat_to_sorted,
+                          int32_t* ws, hipStream_t s) {
+  int nbits = 1;
+  while ((1 << nbits) < pl.G) ++nbits;
+  if (pl.blocks > 0)
+    seg_count_kernel<<<pl.blocks, kPermThreads, 0, s>>>(topk_idx, src_block, E, k, pl.R, pl.G, pl.chunk, ws);
+  seg_scan_kernel<<<1, kMaxSegments, 0, s>>>(pl.G, pl.blocks, pl.R, ws, counts, offsets);
+  if (pl.blocks > 0)
+    seg_rank_kernel<<<pl.blocks, kPermThreads, 0, s>>>(topk_idx, src_block, E, k, pl.R, pl.G, pl.chunk, nbits, ws,
+                                                       sorted_to_flat, flat_to_sorted);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------ dispatch ---
+// Each token row is read once and written to its k sorted positions,
+// 16 bytes per lane; a block walks whole rows so the writes of one row are
+// contiguous.
+constexpr int kCopyThreads = 256;
+constexpr int kCopyUnroll = 4;
+
+__global__ __launch_bounds__(kCopyThreads) void dispatch_copy_kernel(const uint4* __restrict__ x, int64_t M, int C,
+                                                                     int k, const int32_t* __restrict__ f2s,
+                                                                     uint4* __restrict__ xp) {
+  for (int64_t t = blockIdx.x; t < M; t += gridDim.x) {
+    const uint4* src = x + t * C;
+    for (int c0 = threadIdx.x; c0 < C; c0 += kCopyThreads * kCopyUnroll) {
+      uint4 v[kCopyUnroll];
+#pragma unroll
+      for (int u = 0; u < kCopyUnroll; ++u) {
+        const int c = c0 + u * kCopyThreads;
+        if (c < C) v[u] = src[c];
+      }
+      for (int j = 0; j < k; ++j) {
+        uint4* d = xp + (int64_t)f2s[t * k + j] * C;
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+          const int c = c0 + u * kCopyThreads;
+          if (c < C) d[c] = v[u];
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_dispatch_copy(const void* x, int64_t M, int64_t row_bytes, int k, const int32_t* flat_to_sorted,
+                                void* x_perm, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  const int C = (int)(row_bytes / 16);
+  const int64_t grid = M < 16384 ? M : 16384;
+  dispatch_copy_kernel<<<(unsigned)grid, kCopyThreads, 0, s>>>((const uint4*)x, M, C, k, flat_to_sorted,
+                                                               (uint4*)x_perm);
+  return hipGetLastError();
+}
+
+}  // namespace moe

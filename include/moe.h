@@ -1,0 +1,215 @@
+/*
+ * moe.h -- C ABI of the MoE layer hot path on AMD Instinct MI355X (gfx950).
+ *
+ * One MoE layer, in the order the pages state it:
+ *   route     top-k expert choice per token and renormalised weights
+ *   dispatch  count rows per (source block, expert), prefix-sum offsets,
+ *             stable permutation, gather of token rows sorted by segment
+ *   grouped   Layer0: gate/up products + SwiGLU; Layer1: down product,
+ *   GEMM      both as one grouped GEMM over all experts
+ *   combine   top-k weighted reduction of each token's expert outputs
+ *   layer     all of the above, with the dispatch copy and the combine done
+ *             by dedicated workgroups beside the matrix-core workgroups
+ *
+ * Sources (cited by page and section):
+ *   [COMET]  "COMET: Fine-grained Computation-communication Overlapping for
+ *            Mixture-of-Experts" (paper review): §3.2 Layer0/Layer1
+ *            pipelines; §4.1.1 shared-tensor decomposition (Layer0 along M,
+ *            Layer1 along N because of the Top-K reduction); §4.1.2
+ *            rescheduling (reorder by source, column-wise GroupGEMM);
+ *            §4.2.1 thread-block specialisation; §4.2.2 adaptive
+ *            thread-block allocation from profiled metadata.
+ *   [GGEMM]  "Grouped GEMM 为什么适合 MoE" (why grouped GEMM suits MoE):
+ *            C_i = A_i B_i over G problems, tile queue, double buffering,
+ *            L2 locality, fused epilogue.
+ *   [PTO]    "PTO MoE算子实战" (PTO MoE operator article): the seven serial
+ *            stages (reorder, AllToAll, reorder, GMM1/SwiGLU/GMM2, reorder,
+ *            AllToAllV, top-K weighted accumulation); MegaMoE fusion;
+ *            count-as-flag.
+ *
+ * Conventions for every call:
+ *   - Tensor arguments are DEVICE pointers to row-major, contiguous memory,
+ *     16-byte aligned (except topk/int32 arrays: 4-byte aligned).  The caller
+ *     allocates and owns every buffer; the library allocates nothing per call
+ *     and keeps no per-call state.
+ *   - `stream` is a hipStream_t (passed as void*); NULL means the default
+ *     stream.  Every call only enqueues work on `stream` and returns; none
+ *     synchronises the device or copies device memory to the host.
+ *   - Errors: arguments are checked on the host; a failed check returns a
+ *     status and enqueues nothing.  Device-resident inputs are trusted:
+ *     logits must be finite, src_block values must lie in [0, S), topk_idx
+ *     in [0, E), and offsets must be the exclusive prefix sum of the counts
+ *     of the same call sequence.  Violating these is undefined behaviour.
+ *   - Symbols: M tokens, H hidden, F expert width, E experts, k = topk,
+ *     S source blocks, G = S*E segments, R = M*k routed rows.
+ *   - Weight storage: W_gate, W_up stored [E,F,H] and W_down stored [E,H,F]:
+ *     row f of W_gate[e] is column f of the H x F matrix of the math
+ *     (x W_gate), so every stored row is contiguous in the reduction index.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, misalignment */
+  MOE_ERR_UNSUPPORTED = 2,      /* valid but outside what the kernels handle */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+  MOE_ERR_HIP = 4,              /* a HIP runtime call failed (launch error) */
+  MOE_ERR_DEVICE_TIMEOUT = 5    /* a bounded device wait ran out (fused layer) */
+} moe_status_t;
+
+typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype_t;
+
+/* Operation whose workspace moe_workspace_bytes sizes. */
+typedef enum { MOE_OP_DISPATCH = 0, MOE_OP_GROUPED_GEMM = 1, MOE_OP_LAYER = 2 } moe_op_t;
+
+/*
+ * Problem shape.  Limits: 0 <= M, M*k < 2^31; H and F multiples of 64 in
+ * [64, 65536]; 1 <= E <= 512; 1 <= k <= min(E, 16); S >= 1, S*E <= 1024;
+ * R*max(H,F) < 2^31 and E*H*F < 2^31 (32-bit element offsets).
+ * dtype is the type of x, the weights, X_perm and Hact: MOE_DTYPE_BF16
+ * (fp32 accumulation) or MOE_DTYPE_F32.  Logits, weights of the top-k, Y and
+ * out are always f32.
+ */
+typedef struct {
+  int64_t num_tokens;     /* M */
+  int32_t hidden;         /* H */
+  int32_t ffn;            /* F */
+  int32_t num_experts;    /* E */
+  int32_t topk;           /* k */
+  int32_t num_src_blocks; /* S (1 unless rows arrive tagged by source block) */
+  int32_t dtype;          /* moe_dtype_t */
+} moe_problem_t;
+
+/* Bytes of device workspace `op` needs for this problem (0 if none).
+ * Returns 0 and sets nothing for an invalid problem; check with the call. */
+size_t moe_workspace_bytes(const moe_problem_t* p, int32_t op);
+
+/*
+ * Route ([COMET] §4.1.1 Top-K reduction; [PTO] seven stages, top-K weighted
+ * accumulation).  For each token t: topk_idx[t, 0..k-1] = the k experts with
+ * the largest logits[t, :], in descending order of logit; equal logits go to
+ * the lower expert index (IEEE comparison: -0.0 ties +0.0).
+ * topk_w[t, j] = exp(l_j - l_0) / sum_{i<k} exp(l_i - l_0), summed in slot
+ * order (softmax over the chosen logits, f32 arithmetic, full-precision exp).
+ *   logits   [M,E] f32 (finite), read only
+ *   topk_idx [M,k] int32, written
+ *   topk_w   [M,k] f32, written
+ */
+moe_status_t moe_route(const moe_problem_t* p, const float* logits, int32_t* topk_idx, float* topk_w, void* stream);
+
+/*
+ * Dispatch ([PTO] local reorder by expert + count-as-flag counts; [COMET]
+ * §4.1.2 reorder by source; §3.2 Layer0 dispatch).  Pair f = t*k + j belongs
+ * to segment g = src_block[t]*E + topk_idx[t,j] (src_block NULL means S = 1).
+ *   counts[g]          number of pairs in segment g                 [G] int32
+ *   offsets            exclusive prefix sum of counts, offsets[G]=R [G+1] int32
+ *   sorted_to_flat[r]  the pair at sorted position r: segments in order,
+ *                      increasing f inside a segment (stable)       [R] int32
+ *   flat_to_sorted     the inverse permutation                     [R] int32
+ *   x_perm[r, :]       = x[sorted_to_flat[r] / k, :]  (byte copy)   [R,H] dtype
+ *   x                  [M,H] dtype, read only
+ * Results are bit-exact and independent of scheduling (no atomics decide
+ * an order).  ws must hold moe_workspace_bytes(p, MOE_OP_DISPATCH) bytes.
+ */
+moe_status_t moe_dispatch(const moe_problem_t* p, const void* x, const int32_t* topk_idx, const int32_t* src_block,
+                          int32_t* counts, int32_t* offsets, int32_t* sorted_to_flat, int32_t* flat_to_sorted,
+                          void* x_perm, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Grouped GEMM over the G segments ([GGEMM] C_i = A_i B_i with per-problem
+ * sizes; segment g uses expert g % E and rows offsets[g] .. offsets[g+1]-1).
+ *   layer 0 ([COMET] §3.2 Layer0; [PTO] GMM1 -> SwiGLU):
+ *     a  = X_perm [R,H] dtype; w0 = W_gate [E,F,H]; w1 = W_up [E,F,H]
+ *     c  = Hact [R,F] dtype: Hact[r,f] = silu(g) * u rounded to dtype, where
+ *          g = sum_h X_perm[r,h] W_gate[e,f,h], u likewise with W_up, both
+ *          accumulated in f32, silu(z) = z / (1 + exp(-z)).
+ *   layer 1 ([COMET] §3.2 Layer1; [PTO] GMM2):
+ *     a  = Hact [R,F] dtype; w0 = W_down [E,H,F]; w1 = NULL
+ *     c  = Y [R,H] f32: Y[r,n] = sum_f Hact[r,f] W_down[e,n,f], f32 accumulation.
+ *   offsets [G+1] int32 as produced by moe_dispatch.  Rows of empty segments
+ *   produce nothing.  ws may be NULL (moe_workspace_bytes returns 0).
+ */
+moe_status_t moe_grouped_gemm(const moe_problem_t* p, int32_t layer, const void* a, const void* w0, const void* w1,
+                              const int32_t* offsets, void* c, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Combine ([COMET] §4.1.1/§4.1.2 Top-K reduction, column-wise; [PTO] Combine
+ * + Unpermute, top-K weighted accumulation).
+ *   out[t, n] = sum_{j=0..k-1} topk_w[t,j] * y[flat_to_sorted[t*k+j], n],
+ *   f32, accumulated from zero in slot order j = 0..k-1 (fused multiply-add).
+ *   y [R,H] f32; topk_w [M,k] f32; flat_to_sorted [R] int32; out [M,H] f32.
+ */
+moe_status_t moe_combine(const moe_problem_t* p, const float* y, const float* topk_w, const int32_t* flat_to_sorted,
+                         float* out, void* stream);
+
+/* Optional device buffers that receive moe_layer's intermediates (any field
+ * may be NULL, then the workspace holds that intermediate). */
+typedef struct {
+  int32_t* topk_idx;       /* [M,k] */
+  float* topk_w;           /* [M,k] */
+  int32_t* counts;         /* [G] */
+  int32_t* offsets;        /* [G+1] */
+  int32_t* sorted_to_flat; /* [R] */
+  int32_t* flat_to_sorted; /* [R] */
+  void* x_perm;            /* [R,H] dtype */
+  void* hact;              /* [R,F] dtype */
+  float* y;                /* [R,H] f32 */
+} moe_layer_aux_t;
+
+/* Schedule options of the fused layer (NULL = defaults).  Results do not
+ * depend on them: every output element is computed in a fixed order. */
+typedef struct {
+  int32_t n_mover;     /* workgroups that copy and combine; <0: from the profiled split table */
+  int32_t grid;        /* total persistent workgroups; <=0: every CU, one each */
+  int32_t fused;       /* 0: run the unfused kernel chain instead of the fused kernel */
+  int32_t spin_limit;  /* >0: bound on each device wait (polls); 0: default bound */
+} moe_layer_opts_t;
+
+/*
+ * The whole layer ([COMET] §4.2.1 thread-block specialisation, §4.2.2
+ * adaptive allocation; [PTO] MegaMoE seven-stage fusion): route, dispatch,
+ * Layer0, Layer1 and combine.  The fused kernel runs n_mover "mover"
+ * workgroups that gather token rows tile by tile and later combine each
+ * column chunk as soon as its Layer1 tiles are done, beside matrix-core
+ * workgroups that take Layer0 then Layer1 tiles from one ordered queue;
+ * per-tile counters in the workspace act as ready flags.  The output equals,
+ * bit for bit, the unfused chain moe_route -> moe_dispatch ->
+ * moe_grouped_gemm(0) -> moe_grouped_gemm(1) -> moe_combine.
+ *   x [M,H] dtype; logits [M,E] f32; src_block [M] int32 or NULL (S = 1);
+ *   w_gate, w_up [E,F,H]; w_down [E,H,F]; out [M,H] f32.
+ * If a bounded device wait runs out, the kernel stops early and records
+ * MOE_ERR_DEVICE_TIMEOUT in the workspace; read it with
+ * moe_debug_device_status.
+ */
+moe_status_t moe_layer(const moe_problem_t* p, const void* x, const float* logits, const int32_t* src_block,
+                       const void* w_gate, const void* w_up, const void* w_down, float* out,
+                       const moe_layer_aux_t* aux, const moe_layer_opts_t* opts, void* ws, size_t ws_bytes,
+                       void* stream);
+
+/* Mover workgroups the profiled split table picks for this problem (the
+ * value moe_layer uses when opts->n_mover < 0), or -1 for an invalid problem. */
+int32_t moe_layer_default_movers(const moe_problem_t* p);
+
+/* Synchronises `stream` and returns the device status the last moe_layer
+ * on this workspace recorded (MOE_OK or MOE_ERR_DEVICE_TIMEOUT).  Tests only. */
+moe_status_t moe_debug_device_status(const moe_problem_t* p, void* ws, size_t ws_bytes, void* stream);
+
+/* Human-readable name of a status. */
+const char* moe_status_string(moe_status_t s);
+
+/* ABI version: (major << 16) | minor. */
+int32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

@@ -1,0 +1,112 @@
+"""The C-ABI library loads and exports every symbol include/moe.h declares,
+and rejects bad arguments on the host (CPU only: no call here reaches a
+kernel launch)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import combine_topk_gate_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(moe.LIB_PATH):
+        from combine_topk_gate_amd import build
+        build.build()
+    return moe.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert "moe_layer" in names and "moe_route" in names and len(names) >= 10
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (moe_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        getattr(lib, n)
+    assert set(moe.EXPORTED) == set(names)
+
+
+def test_no_torch_types_in_header():
+    text = open(HEADER).read()
+    assert "torch" not in text.lower().replace("torch", "", 0) or "at::" not in text
+    assert "at::Tensor" not in text and "c10" not in text
+
+
+def test_version_and_status_strings(lib):
+    assert moe.moe_abi_version() >> 16 == 1
+    assert moe.moe_status_string(moe.MOE_OK) == "MOE_OK"
+    assert moe.moe_status_string(moe.MOE_ERR_DEVICE_TIMEOUT) == "MOE_ERR_DEVICE_TIMEOUT"
+
+
+BAD = [
+    dict(M=-1), dict(H=100), dict(H=0), dict(F=32), dict(E=0), dict(E=513), dict(k=0), dict(k=17),
+    dict(E=4, k=5), dict(S=0), dict(S=3, E=512), dict(dtype=7),
+]
+
+
+@pytest.mark.parametrize("bad", BAD)
+def test_invalid_problem_is_rejected_without_launch(lib, bad):
+    shape = dict(M=16, H=64, F=64, E=8, k=2, S=1, dtype=moe.MOE_DTYPE_BF16)
+    shape.update(bad)
+    p = moe.Problem(shape["M"], shape["H"], shape["F"], shape["E"], shape["k"], shape["S"], shape["dtype"])
+    assert lib.moe_route(ctypes.byref(p), None, None, None, None) == moe.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_workspace_bytes(ctypes.byref(p), moe.MOE_OP_LAYER) == 0
+    assert lib.moe_layer_default_movers(ctypes.byref(p)) == -1
+
+
+def test_null_and_misaligned_pointers_are_rejected(lib):
+    p = moe.problem(16, 64, 64, 8, 2)
+    assert lib.moe_route(None, None, None, None, None) == moe.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_route(ctypes.byref(p), None, None, None, None) == moe.MOE_ERR_INVALID_ARGUMENT
+    fake = ctypes.c_void_p(0x1000)
+    odd = ctypes.c_void_p(0x1002)
+    # misaligned x in dispatch
+    ws = ctypes.c_void_p(0x100000)
+    r = lib.moe_dispatch(ctypes.byref(p), odd, fake, None, fake, fake, fake, fake, fake, ws, 1 << 20, None)
+    assert r == moe.MOE_ERR_INVALID_ARGUMENT
+    # too-small workspace
+    r = lib.moe_dispatch(ctypes.byref(p), fake, fake, None, fake, fake, fake, fake, fake, ws, 0, None)
+    assert r == moe.MOE_ERR_WORKSPACE_TOO_SMALL
+    # source blocks without src_block
+    p8 = moe.problem(16, 64, 64, 8, 2, S=2)
+    r = lib.moe_dispatch(ctypes.byref(p8), fake, fake, None, fake, fake, fake, fake, fake, ws, 1 << 20, None)
+    assert r == moe.MOE_ERR_INVALID_ARGUMENT
+    # grouped gemm: bad layer, missing up weights
+    assert lib.moe_grouped_gemm(ctypes.byref(p), 2, fake, fake, fake, fake, fake, None, 0, None) == \
+        moe.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_grouped_gemm(ctypes.byref(p), 0, fake, fake, None, fake, fake, None, 0, None) == \
+        moe.MOE_ERR_INVALID_ARGUMENT
+    # layer: workspace too small
+    opts = moe.LayerOpts(-1, 0, 1, 0)
+    r = lib.moe_layer(ctypes.byref(p), fake, fake, None, fake, fake, fake, fake, None, ctypes.byref(opts), ws, 16,
+                      None)
+    assert r == moe.MOE_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_unsupported_sizes(lib):
+    # 32-bit element offsets: R * H must stay below 2^31
+    p = moe.problem(1 << 20, 4096, 64, 8, 2)
+    assert lib.moe_route(ctypes.byref(p), None, None, None, None) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_workspace_sizes_cover_intermediates(lib):
+    for (M, H, F, E, k, S) in [(8192, 4096, 14336, 8, 2, 1), (16384, 7168, 4096, 16, 8, 8), (1, 64, 64, 1, 1, 1)]:
+        p = moe.problem(M, H, F, E, k, S)
+        R = M * k
+        need = R * H * 2 + R * F * 2 + R * H * 4 + 4 * R * 4
+        assert moe.moe_workspace_bytes(p, moe.MOE_OP_LAYER) >= need
+        assert moe.moe_workspace_bytes(p, moe.MOE_OP_DISPATCH) >= 4 * S * E
+        assert moe.moe_workspace_bytes(p, moe.MOE_OP_GROUPED_GEMM) == 0

@@ -24,16 +24,21 @@ pytestmark = pytest.mark.gpu
 
 SAMPLE = {"tiny": None, "qwen2": 64, "mixtral": 24, "phi35": 24, "epshare": 16}
 
-_cache = {}
+NAMES = list(SAMPLE)
 
 
-def get_case(name):
-    """Inputs, GPU chain outputs and the oracle for one named layer (one at a time)."""
-    if name in _cache:
-        return _cache[name]
-    _cache.clear()
+@pytest.fixture(scope="module", params=NAMES)
+def case(request):
+    """Inputs, GPU chain outputs and the oracle for one named layer; module
+    scope, so pytest runs every test of one layer before building the next."""
+    c = _build_case(request.param)
+    yield c
+    c.clear()
     gc.collect()
     torch.cuda.empty_cache()
+
+
+def _build_case(name):
     cfg = moe_synth.config(name)
     print(f"[parity] preparing {name} {cfg}", flush=True)
     d = moe_synth.make_inputs(cfg)
@@ -42,24 +47,17 @@ def get_case(name):
     toks = None if SAMPLE[name] is None else moe_synth.token_sample(cfg, SAMPLE[name])
     ref = oracle.moe_layer(d["x"], d["logits"], d["w_gate"], d["w_up"], d["w_down"], cfg.k, S=cfg.S,
                            src_block=d["src_block"], tokens=toks, want_rows=True)
-    case = dict(cfg=cfg, d=d, g=g, out=out, ref=ref, toks=toks)
-    _cache[name] = case
-    return case
+    return dict(name=name, cfg=cfg, d=d, g=g, out=out, ref=ref, toks=toks)
 
 
-NAMES = list(SAMPLE)
-
-
-@pytest.mark.parametrize("name", NAMES)
-def test_route_bit_exact(name):
-    c = get_case(name)
+def test_route_bit_exact(case):
+    c = case
     assert np.array_equal(host(c["out"]["topk_idx"]), c["ref"]["topk_idx"])
     assert np.max(np.abs(host(c["out"]["topk_w"]) - c["ref"]["topk_w"])) <= 1e-6
 
 
-@pytest.mark.parametrize("name", NAMES)
-def test_dispatch_bit_exact(name):
-    c = get_case(name)
+def test_dispatch_bit_exact(case):
+    c = case
     o, r, cfg = c["out"], c["ref"], c["cfg"]
     for key in ("counts", "offsets", "sorted_to_flat", "flat_to_sorted"):
         assert np.array_equal(host(o[key]), r[key]), key
@@ -76,23 +74,29 @@ def _sample_rows(c):
     return r["flat_to_sorted"][flat].astype(np.int64), toks
 
 
-@pytest.mark.parametrize("name", NAMES)
-def test_layer0_swiglu(name):
-    c = get_case(name)
+def test_layer0_swiglu(case):
+    c = case
     rows, _ = _sample_rows(c)
     got = host(c["out"]["hact"][torch.from_numpy(rows).cuda()])
     ref = c["ref"]["hact"]
     if c["cfg"].dtype == "bf16":
-        # one bf16 rounding step at most, anywhere
-        assert np.all(np.abs(got - ref) <= 2.0 ** -7 * np.abs(ref) + 1e-30)
+        # Both sides round silu(g)*u to bf16: one rounding step (2^-8 relative,
+        # 2^-7 across a binade edge) where the f32-accumulated g, u fall on the
+        # other side of a rounding boundary, plus the f32 accumulation error
+        # itself, which only shows where h is near zero (|dg| ~ 1e-6 for
+        # K <= 7168 products of N(0,1) x N(0,0.02^2) terms; bound 5e-5).
+        dev_ = np.abs(got - ref)
+        excess = dev_ - 2.0 ** -7 * np.abs(ref)
+        print(f"[parity] {c['name']}: hact max|d| {dev_.max():.3e}, max excess over 1 ulp {excess.max():.3e}, "
+              f"relF {rel_fro(got, ref):.3e}")
+        assert np.all(excess <= 5e-5)
         assert rel_fro(got, ref) <= 1e-3
     else:
         assert rel_fro(got, ref) <= 1e-5
 
 
-@pytest.mark.parametrize("name", NAMES)
-def test_layer1_down(name):
-    c = get_case(name)
+def test_layer1_down(case):
+    c = case
     rows, _ = _sample_rows(c)
     got = host(c["out"]["y"][torch.from_numpy(rows).cuda()])
     rel, mabs = tolerances(c["cfg"])
@@ -101,22 +105,20 @@ def test_layer1_down(name):
         assert np.max(np.abs(got - c["ref"]["y"])) <= mabs
 
 
-@pytest.mark.parametrize("name", NAMES)
-def test_combine_output(name):
-    c = get_case(name)
+def test_combine_output(case):
+    c = case
     _, toks = _sample_rows(c)
     got = host(c["out"]["out"][torch.from_numpy(toks).cuda()])
     rel, mabs = tolerances(c["cfg"])
     err = rel_fro(got, c["ref"]["out"])
-    print(f"[parity] {name}: out relF {err:.3e} maxabs {np.max(np.abs(got - c['ref']['out'])):.3e}")
+    print(f"[parity] {c['name']}: out relF {err:.3e} maxabs {np.max(np.abs(got - c['ref']['out'])):.3e}")
     assert err <= rel
     if mabs is not None:
         assert np.max(np.abs(got - c["ref"]["out"])) <= mabs
 
 
-@pytest.mark.parametrize("name", NAMES)
-def test_layer_equals_chain_bitwise(name):
-    c = get_case(name)
+def test_layer_equals_chain_bitwise(case):
+    c = case
     out, _, status = run_layer(c["cfg"], c["g"])
     assert status == 0
     assert torch.equal(out, c["out"]["out"])
@@ -145,9 +147,9 @@ EDGE = {
 }
 
 
-@pytest.mark.parametrize("case", list(EDGE))
-def test_edge_case_full_parity(case):
-    kw = dict(EDGE[case])
+@pytest.mark.parametrize("edge", list(EDGE))
+def test_edge_case_full_parity(edge):
+    kw = dict(EDGE[edge])
     bias = kw.pop("bias", None)
     cfg, d = _edge_inputs(**kw, bias=bias)
     g = upload(d)

@@ -40,7 +40,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="mixtral")
-    ap.add_argument("--mode", choices=("chain", "layer"), default="chain")
+    ap.add_argument("--mode", choices=("chain", "layer"), default="layer",
+                    help="layer: moe_layer with the library's per-shape choice; chain: moe_layer forced unfused")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--n-mover", type=int, default=-1)
@@ -114,10 +115,23 @@ def main():
     stream = torch.cuda.current_stream()
     src = g.get("src_block")
 
-    nev = 6
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    def time_steps(fn, nev, warmup, steps):
+        for _ in range(warmup):
+            fn(None)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for i in range(steps):
+            fn(evs[i])
+        t1.record(stream)
+        torch.cuda.synchronize()
+        per = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(nev - 1)]
+                        for i in range(steps)]) * 1e3  # us
+        return t0.elapsed_time(t1) / steps, per
 
-    def step_chain(ev=None):
+    def step_chain(ev):
         if ev: ev[0].record(stream)
         moe.moe_route(p, g["logits"], idx, w, stream)
         if ev: ev[1].record(stream)
@@ -130,27 +144,21 @@ def main():
         moe.moe_combine(p, y, w, f2s, out, stream)
         if ev: ev[5].record(stream)
 
-    def step_layer(ev=None):
+    def step_layer(ev):
         if ev: ev[0].record(stream)
         moe.moe_layer(p, g["x"], g["logits"], src, g["w_gate"], g["w_up"], g["w_down"], out, ws_l,
-                      n_mover=args.n_mover, stream=stream)
-        if ev: ev[5].record(stream)
+                      n_mover=args.n_mover, fused=0 if args.mode == "chain" else 1, stream=stream)
+        if ev: ev[1].record(stream)
 
-    step = step_chain if args.mode == "chain" else step_layer
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    t_start.record(stream)
-    for i in range(args.steps):
-        step(events[i])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms_total = t_start.elapsed_time(t_end)
-    ms_step = ms_total / args.steps
+    # (1) the step: one moe_layer call (the library's per-shape choice of the
+    #     fused kernel or the chain), timed as a whole
+    ms_step, _ = time_steps(step_layer, 2, args.warmup, args.steps)
+    # (2) the same layer as the chain of C-ABI calls, with an event between
+    #     calls: per-step times and the dominant kernel's live duration
+    ms_chain, per = time_steps(step_chain, 6, args.warmup, args.steps)
 
     flops = 6.0 * R * H * F
+    movers = moe.moe_layer_default_movers(p) if args.n_mover < 0 else args.n_mover
     res = {"metric": "MoE layer us + grouped-GEMM TFLOP/s (% MFMA peak), Mixtral shape M=8192",
            "value": flops / (ms_step * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
@@ -158,27 +166,33 @@ def main():
            "data": "synthetic (seeded N(0,1) tokens and logits, N(0,0.02^2) weights, random-init)",
            "config": {"workload": f"{cfg.name}: MoE layer M={M} H={H} F={F} E={cfg.E} topk={k} S={cfg.S}",
                       "tokens": M, "hidden": H, "ffn": F, "experts": cfg.E, "topk": k, "src_blocks": cfg.S,
-                      "mode": args.mode},
-           "layer_us": ms_step * 1e3}
-    if args.mode == "chain":
-        per = np.array([[events[i][j].elapsed_time(events[i][j + 1]) for j in range(nev - 1)]
-                        for i in range(args.steps)]) * 1e3  # us
-        mean = per.mean(axis=0)
-        names = ["route", "dispatch", "gemm_l0", "gemm_l1", "combine"]
-        res["step_us"] = {n: float(v) for n, v in zip(names, mean)}
-        t_gemm = (mean[2] + mean[3]) * 1e-6
-        peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
-        res["grouped_gemm_tflops"] = flops / t_gemm / 1e12
-        res["grouped_gemm_pct_peak"] = 100.0 * res["grouped_gemm_tflops"] / peak
-        disp_bytes = M * H * (2 if cfg.dtype == "bf16" else 4) * (1 + k) + R * 4
-        comb_bytes = R * H * 4 + M * H * 4 + M * k * 8
-        res["dispatch_gbs"] = disp_bytes / (mean[1] * 1e-6) / 1e9
-        res["combine_gbs"] = comb_bytes / (mean[4] * 1e-6) / 1e9
-        l0_flops = 4.0 * R * H * F
-        ach = l0_flops / (mean[2] * 1e-6) / 1e12
-        res["roofline"] = {"kernel": "grouped_gemm_bf16_kernel<0> (Layer0 gate/up + SwiGLU)", "bound": "mfma",
-                           "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak, "traffic": None,
-                           "launch_us": float(mean[2]), "algorithmic": f"4*R*H*F = {l0_flops:.4g} flop per launch"}
+                      "layer_call": "fused" if (args.mode == "layer" and movers > 0 and cfg.dtype == "bf16")
+                      else "chain", "n_mover": movers},
+           "layer_us": ms_step * 1e3, "chain_us": ms_chain * 1e3}
+    mean = per.mean(axis=0)
+    names = ["route", "dispatch", "gemm_l0", "gemm_l1", "combine"]
+    res["step_us"] = {n: float(v) for n, v in zip(names, mean)}
+    t_gemm = (mean[2] + mean[3]) * 1e-6
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    res["grouped_gemm_tflops"] = flops / t_gemm / 1e12
+    res["grouped_gemm_pct_peak"] = 100.0 * res["grouped_gemm_tflops"] / peak
+    eb = 2 if cfg.dtype == "bf16" else 4
+    disp_bytes = M * H * eb * (1 + k) + R * 4
+    comb_bytes = R * H * 4 + M * H * 4 + M * k * 8
+    res["dispatch_gbs"] = disp_bytes / (mean[1] * 1e-6) / 1e9
+    res["combine_gbs"] = comb_bytes / (mean[4] * 1e-6) / 1e9
+    res["dispatch_pct_hbm"] = 100.0 * res["dispatch_gbs"] / PEAK_HBM_GBS
+    res["combine_pct_hbm"] = 100.0 * res["combine_gbs"] / PEAK_HBM_GBS
+    # single-GPU analogue of hidden communication: the share of the data
+    # movement (dispatch + combine) that the fused step hides behind the GEMMs
+    move = mean[1] + mean[4]
+    res["movement_hidden_pct"] = 100.0 * (1.0 - (ms_step * 1e3 - mean[0] - mean[2] - mean[3]) / move)
+    l0_flops = 4.0 * R * H * F
+    ach = l0_flops / (mean[2] * 1e-6) / 1e12
+    res["roofline"] = {"kernel": "grouped_gemm_bf16_kernel<0> (Layer0 gate/up + SwiGLU), chain timing",
+                       "bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak,
+                       "traffic": None, "launch_us": float(mean[2]),
+                       "algorithmic": f"4*R*H*F = {l0_flops:.4g} flop per launch"}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, d, args.cpu_seconds)
     print(json.dumps(res))

@@ -175,7 +175,7 @@ moe_status_t moe_combine(const moe_problem_t* p, const float* y, const float* to
 }
 
 int32_t moe_layer_default_movers(const moe_problem_t* p) {
-  if (check_problem(p) != MOE_OK) return -1;
+  if (check_problem(p) != MOE_OK || p->dtype != MOE_DTYPE_BF16) return -1;
   return fused_default_movers(p->num_tokens, p->hidden, p->ffn, p->num_experts, p->topk, p->num_src_blocks,
                               p->dtype, device_cu_count());
 }
@@ -239,10 +239,11 @@ moe_status_t moe_layer(const moe_problem_t* p, const void* x, const float* logit
   if (e != hipSuccess) return MOE_ERR_HIP;
 
   const int cus = device_cu_count();
+  // n_mover < 0 asks the profiled table, which may pick the kernel chain
   const int movers = o.n_mover >= 0 ? o.n_mover
                                     : fused_default_movers(M, p->hidden, p->ffn, p->num_experts, p->topk,
                                                            p->num_src_blocks, p->dtype, cus);
-  const bool fused = o.fused != 0 && p->dtype == MOE_DTYPE_BF16 && movers > 0;
+  const bool fused = o.fused != 0 && p->dtype == MOE_DTYPE_BF16 && movers >= 0;
   if (fused) {
     FusedArgs fa;
     fa.M = M;
@@ -259,17 +260,23 @@ moe_status_t moe_layer(const moe_problem_t* p, const void* x, const float* logit
     fa.offsets = offsets;
     fa.s2f = s2f;
     fa.f2s = f2s;
-    fa.x_perm = xp;
     fa.hact = hact;
     fa.y = y;
     fa.out = out;
     fa.status = status;
     fa.flags = at<int32_t>(ws, L.fused);
+    fa.mt_max = fused_mt_max(M, p->hidden, p->topk, G);
     fa.grid = o.grid > 0 ? o.grid : cus;
     fa.n_mover = movers;
     fa.spin_limit = o.spin_limit;
     moe_status_t fs = fused_check(fa, cus);
     if (fs != MOE_OK) return fs;
+    // the fused kernel reads token rows straight from x; X_perm is produced
+    // only when the caller asks for it
+    if (a.x_perm) {
+      e = launch_dispatch_copy(x, M, (int64_t)p->hidden * elem_bytes(p), p->topk, f2s, xp, s);
+      if (e != hipSuccess) return MOE_ERR_HIP;
+    }
     return hip_status(launch_fused_layer(fa, s));
   }
   e = launch_dispatch_copy(x, M, (int64_t)p->hidden * elem_bytes(p), p->topk, f2s, xp, s);

@@ -43,11 +43,16 @@ constexpr int kL1Cols = 256;                       // Y columns per layer-1 tile
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
 struct Bf16GemmArgs {
-  const __bf16* a;   // token rows [R, K]
+  const __bf16* a;   // token rows [R, K]; gather mode: token-major x [M, K]
   const __bf16* w0;  // layer 0: W_gate [E, F, H]; layer 1: W_down [E, H, F]
   const __bf16* w1;  // layer 0: W_up [E, F, H]
   void* c;           // layer 0: Hact [R, F] bf16; layer 1: Y [R, H] f32
   int K, N, E;
+  // gather mode (layer 0 inside the fused layer): sorted row r reads token
+  // row sorted_to_flat[r] / topk of x directly, so X_perm is never written
+  const int32_t* s2f;
+  int topk;
+  int64_t M;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -58,9 +63,18 @@ __device__ __forceinline__ i32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t
   return __builtin_bit_cast(i32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
 }
 
-template <int LAYER>
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+template <int LAYER, bool GATHER = false>
 __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int seg_start, int seg_rows, int m0,
                                                int nt, char* __restrict__ lds) {
+  // tile coordinates come from LDS; make them provably wave-uniform so the
+  // buffer descriptors live in SGPRs (no per-lane descriptor loops)
+  g = uniform(g);
+  seg_start = uniform(seg_start);
+  seg_rows = uniform(seg_rows);
+  m0 = uniform(m0);
+  nt = uniform(nt);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wn = wave & 1, wm = wave >> 1;
@@ -83,29 +97,45 @@ __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int
     rw1 = rw0;
   }
   const int trows = min(seg_rows - m0, kTileRows);
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(p.a + (int64_t)(seg_start + m0) * K, (uint32_t)trows * row_bytes);
-
   const uint32_t voff0 = (uint32_t)lr * row_bytes + (uint32_t)lc * 16u;
   const uint32_t vstep = 32u * row_bytes;
-  const uint32_t st_off = (uint32_t)lr * 128u + ((uint32_t)(lc ^ (lr & 7)) << 4);
-
-  i32x4_t wreg[8], xreg[8];
-  auto gload = [&](int kt) {
-    const uint32_t soff = (uint32_t)kt * (kBK * 2);
+  __amdgpu_buffer_rsrc_t rx;
+  uint32_t xvoff[8];
+  if (GATHER) {
+    // token rows of x; rows past the segment end read zeros (offset past the range)
+    rx = make_rsrc(p.a, (uint32_t)(p.M * (int64_t)row_bytes));
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
+      const int r = lr + 32 * i;
+      xvoff[i] = 0x80000000u;
+      if (r < trows) xvoff[i] = (uint32_t)(p.s2f[seg_start + m0 + r] / p.topk) * row_bytes + (uint32_t)lc * 16u;
+    }
+  } else {
+    rx = make_rsrc(p.a + (int64_t)(seg_start + m0) * K, (uint32_t)trows * row_bytes);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xvoff[i] = voff0 + (uint32_t)i * vstep;
+  }
+  const uint32_t st_off = (uint32_t)lr * 128u + ((uint32_t)(lc ^ (lr & 7)) << 4);
+
+  // Global loads in 4 parts (one per k16 sub-step of the MFMA loop); part q
+  // covers the thread's rows lr + 32 i for i in {2q, 2q+1}, weights and tokens.
+  i32x4_t wreg[8], xreg[8];
+  auto gload_part = [&](int kt, int q) {
+    const uint32_t soff = (uint32_t)kt * (kBK * 2);
+#pragma unroll
+    for (int i = 2 * q; i < 2 * q + 2; ++i) {
       if (LAYER == 0)
         wreg[i] = buf_load16(i < 4 ? rw0 : rw1, voff0 + (uint32_t)(i & 3) * vstep, soff);
       else
         wreg[i] = buf_load16(rw0, voff0 + (uint32_t)i * vstep, soff);
-      xreg[i] = buf_load16(rx, voff0 + (uint32_t)i * vstep, soff);
+      xreg[i] = buf_load16(rx, xvoff[i], soff);
     }
   };
-  auto lstore = [&](int stage) {
+  auto lstore_part = [&](int stage, int q) {
     char* wdst = lds + stage * kStageBytes + st_off;
     char* xdst = wdst + kOperandBytes;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 2 * q; i < 2 * q + 2; ++i) {
       *reinterpret_cast<i32x4_t*>(wdst + i * 4096) = wreg[i];
       *reinterpret_cast<i32x4_t*>(xdst + i * 4096) = xreg[i];
     }
@@ -113,18 +143,30 @@ __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int
 
   // ---- fragment addressing
   const int lrow = lane & 31, lk = lane >> 5;
-  int wrow[4];
+  uint32_t wrow_off[4];
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
-    if (LAYER == 0)
-      wrow[mi] = (mi < 2 ? wn * 64 + mi * 32 : 128 + wn * 64 + (mi - 2) * 32) + lrow;
-    else
-      wrow[mi] = wn * 128 + mi * 32 + lrow;
+    const int r = (LAYER == 0) ? (mi < 2 ? wn * 64 + mi * 32 : 128 + wn * 64 + (mi - 2) * 32) + lrow
+                               : wn * 128 + mi * 32 + lrow;
+    wrow_off[mi] = (uint32_t)r * 128u;
   }
-  const int xrow0 = wm * 128 + lrow;
+  const uint32_t xrow_off = (uint32_t)(kOperandBytes + (wm * 128 + lrow) * 128);
   uint32_t kswz[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) kswz[ks] = (uint32_t)(((2 * ks + lk) ^ (lrow & 7)) << 4);
+
+  // two register sets of fragments: sub-step ks uses set ks & 1 while the
+  // reads for ks + 1 fill the other set
+  bf16x8_t fa[2][4], fb[2][4];
+  auto read_frags = [&](int set, int stage, int ks) {
+    const char* base = lds + stage * kStageBytes;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+      fa[set][mi] = *reinterpret_cast<const bf16x8_t*>(base + wrow_off[mi] + kswz[ks]);
+#pragma unroll
+    for (int nj = 0; nj < 4; ++nj)
+      fb[set][nj] = *reinterpret_cast<const bf16x8_t*>(base + xrow_off + nj * 4096 + kswz[ks]);
+  };
 
   f32x16_t acc[4][4];
 #pragma unroll
@@ -134,35 +176,102 @@ __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mi][nj][v] = 0.0f;
 
-  const int nk = K / kBK;
-  gload(0);
-  lstore(0);
-  if (nk > 1) gload(1);
-  __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const char* wsrc = lds + (kt & 1) * kStageBytes;
-    const char* xsrc = wsrc + kOperandBytes;
+  auto mfma_step = [&](int set) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      bf16x8_t af[4], bfr[4];
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-        af[mi] = *reinterpret_cast<const bf16x8_t*>(wsrc + wrow[mi] * 128 + kswz[ks]);
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
       for (int nj = 0; nj < 4; ++nj)
-        bfr[nj] = *reinterpret_cast<const bf16x8_t*>(xsrc + (xrow0 + nj * 32) * 128 + kswz[ks]);
+        acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][mi], fb[set][nj], acc[mi][nj], 0, 0, 0);
+  };
+
+  const int nk = K / kBK;
+  // prologue: stage 0 into LDS, stage 1 into registers, fragments of (0, 0)
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+  for (int q = 0; q < 4; ++q) gload_part(0, q);
 #pragma unroll
-        for (int nj = 0; nj < 4; ++nj)
-          acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[nj], acc[mi][nj], 0, 0, 0);
+  for (int q = 0; q < 4; ++q) lstore_part(0, q);
+  const int k1 = nk > 1 ? 1 : 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) gload_part(k1, q);
+  __syncthreads();
+  read_frags(0, 0, 0);
+
+  // Main loop.  Iteration kt computes stage kt from LDS buffer kt & 1 while
+  // (a) the registers holding stage kt+1 drain into the other buffer and
+  // (b) the registers refill with stage kt+2 from HBM/L2, a quarter per
+  // sub-step, so neither the LDS writes nor the loads sit in one burst.
+  // The barrier comes before the last sub-step's MFMAs: the reads of the
+  // next stage's first fragments are then in flight while those MFMAs run.
+  // The last iteration's stores, loads and reads run too (on a clamped, valid
+  // slice into the idle buffer) so the loop body has no branches; every LDS
+  // access of the tile precedes its last barrier, so the next tile's
+  // prologue may overwrite either buffer.
+  //
+  // One wave per SIMD cannot hide an LDS read behind another wave, so the
+  // order inside each k16 sub-step is pinned with scheduling groups: the 16
+  // MFMAs of sub-step ks alternate with the 8 fragment reads of ks + 1, the
+  // 4 LDS stores of stage kt+1 and the 4 loads of stage kt+2.  In the last
+  // sub-step the barrier sits after 8 of the 16 MFMAs, and the first reads
+  // of stage kt+1 go out between the remaining 8.
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1, nxt = cur ^ 1;
+    const int kload = (kt + 2 < nk) ? kt + 2 : nk - 1;
+#pragma unroll
+    for (int ks = 0; ks < 3; ++ks) {
+      read_frags((ks + 1) & 1, cur, ks + 1);
+      lstore_part(nxt, ks);
+      gload_part(kload, ks);
+      mfma_step(ks & 1);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (kt + 1 < nk) {
-      lstore((kt + 1) & 1);
-      if (kt + 2 < nk) gload(kt + 2);
+    // sub-step 3: first half of the MFMAs with the last stores and loads
+    lstore_part(nxt, 3);
+    gload_part(kload, 3);
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int nj = 0; nj < 4; ++nj)
+        acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][mi], fb[1][nj], acc[mi][nj], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+    }
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(0, nxt, 0);
+#pragma unroll
+    for (int mi = 2; mi < 4; ++mi)
+#pragma unroll
+      for (int nj = 0; nj < 4; ++nj)
+        acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][mi], fb[1][nj], acc[mi][nj], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // ---- epilogue: lane holds column block 8q + 4 lk + (0..3) of token row lrow

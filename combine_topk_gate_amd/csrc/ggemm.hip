@@ -13,13 +13,6 @@
 
 namespace moe {
 
-struct TileLds {
-  int seg_start[kMaxTileSegs + 1];
-  int seg_rows[kMaxTileSegs + 1];
-  int tile_start[kMaxTileSegs + 1];
-  int scratch[kGemmThreads];
-};
-
 template <int LAYER>
 __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(Bf16GemmArgs args,
                                                                          const int32_t* __restrict__ offsets, int G,
@@ -27,10 +20,10 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(Bf16Gem
   __shared__ __attribute__((aligned(16))) char lds[kGemmLdsBytes];
   __shared__ TileLds tl;
   const int NT = (args.N + (LAYER == 0 ? kL0Cols : kL1Cols) - 1) / (LAYER == 0 ? kL0Cols : kL1Cols);
-  const int total = build_tile_table(offsets, G, NT, kTileRows, tl.seg_start, tl.seg_rows, tl.tile_start, tl.scratch);
+  const int total = build_tile_table(offsets, G, kTileRows, tl) * NT;
   const int grid = gridDim.x;
   for (int v = xcd_slot(blockIdx.x, grid); v < total; v += grid) {
-    const TileCoord c = tile_coord(v, G, NT, kTileRows, group_cols, tl.seg_rows, tl.tile_start);
+    const TileCoord c = tile_coord(v, G, NT, kTileRows, group_cols, tl);
     bf16_gemm_tile<LAYER>(args, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], c.m0, c.nt, lds);
   }
 }
@@ -51,15 +44,14 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(const float* __re
                                                                int G) {
   __shared__ float xs[kF32Rows][kF32BK + 1];
   __shared__ float ws[kF32Rows][kF32BK + 1];
-  __shared__ int seg_start[kMaxTileSegs + 1], seg_rows[kMaxTileSegs + 1], tile_start[kMaxTileSegs + 1];
-  __shared__ int scratch[256];
+  __shared__ TileLds tl;
   constexpr int cols = (LAYER == 0) ? kF32Rows / 2 : kF32Rows;
   const int NT = (N + cols - 1) / cols;
-  const int total = build_tile_table(offsets, G, NT, kF32Rows, seg_start, seg_rows, tile_start, scratch);
+  const int total = build_tile_table(offsets, G, kF32Rows, tl) * NT;
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   for (int v = blockIdx.x; v < total; v += gridDim.x) {
-    const TileCoord c = tile_coord(v, G, NT, kF32Rows, 1, seg_rows, tile_start);
-    const int e = c.g % E, s0 = seg_start[c.g], nrows = seg_rows[c.g];
+    const TileCoord c = tile_coord(v, G, NT, kF32Rows, 1, tl);
+    const int e = c.g % E, s0 = tl.seg_start[c.g], nrows = tl.seg_rows[c.g];
     const int col0 = c.nt * cols;
     const int64_t ebase = (int64_t)e * N * K;
     float acc[4][4] = {};
@@ -140,6 +132,9 @@ hipError_t launch_grouped_gemm_bf16(const GemmProblem& gp, hipStream_t s) {
   a.K = gp.K;
   a.N = gp.N;
   a.E = gp.E;
+  a.s2f = nullptr;
+  a.topk = 1;
+  a.M = 0;
   const int grid = device_cu_count();
   const int group_cols = grid / kXcds > 0 ? grid / kXcds : 1;
   if (gp.layer == 0)

@@ -1,7 +1,51 @@
-// Fused MoE layer: placeholder until the fused kernel lands; the layer runs
-// the kernel chain (route, permute, dispatch, grouped GEMM x2, combine).
+// Fused MoE layer: one persistent kernel, one ordered work queue.
+//
+// COMET paper review §4.2.1 (thread-block specialisation: data movement and
+// GEMM in different thread blocks, the GEMM blocks keep the unfused GEMM
+// code) and §4.2.2 (adaptive allocation: the best split depends on the
+// shape, is profiled ahead of time and looked up at run time); §4.1.1-§4.1.2
+// (Layer0's shared tensor is consumed per M tile; Layer1's per column chunk
+// because the Top-K reduction couples a token's rows; the GroupGEMM runs
+// column chunk by column chunk so the reduction of the first chunks starts
+// early).  PTO MoE article: the seven stages in one kernel, stage hand-offs
+// through ready counters with no global barrier, and the number of cores on
+// each stage changing while the kernel runs (dynamic AIC grouping).
+//
+// On one GPU the pages' communication becomes HBM traffic: the gather of
+// token rows and the scatter-reduce of expert outputs.  A handful of
+// workgroups cannot drive HBM (a copy needs many CUs' worth of loads in
+// flight), so the gather is not a separate stage here: Layer0 tiles read
+// their token rows straight from x through sorted_to_flat (the GEMM loads
+// the rows anyway), and X_perm is never written.  What remains is the
+// combine, which runs on workgroups chosen in one of two ways:
+//   n_mover > 0  workgroups [0, n_mover) are dedicated combiners: they take
+//                combine items (column chunk c, block of 32 tokens) in
+//                order, each as soon as chunk c's Layer1 tiles are done;
+//   n_mover = 0  the combine items sit in the single work queue right after
+//                the Layer1 tiles of the next chunk, so whichever
+//                workgroup reaches them does them -- the number of
+//                workgroups moving data grows when the matrix work runs out.
+// The queue: every Layer0 tile; then per column chunk c its Layer1 tiles
+// (each waits until all Layer0 column tiles of its M-tile are done),
+// followed (dynamic mode) by the combine items of chunk c-1; finally the
+// combine items of the last chunk.  Items are claimed with an atomic
+// counter in queue order and every wait targets items earlier in that
+// order, held by resident workgroups, so the kernel cannot deadlock when
+// the whole grid is resident (one workgroup per CU).  Counters in the
+// workspace are the flags: l0done[mt] (Layer0 column tiles of M-tile mt
+// finished) and chunkdone[c] (Layer1 tiles of chunk c finished).
+// Producers publish with an agent-scope release; consumers spin (bounded)
+// and acquire.  A wait that exceeds its bound records a timeout in the
+// status word; every workgroup then stops.
+//
+// Results are bit-identical to the kernel chain: the tiles run the same
+// tile routine on the same values in the same k order, and the combine
+// uses the same per-element routine.
 #include "common.hpp"
+#include "gemm_bf16.hpp"
+#include "launch.hpp"
 #include "layer.hpp"
+#include "tiles.hpp"
 
 namespace moe {
 
@@ -18,12 +62,276 @@ hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
   return hipGetLastError();
 }
 
-size_t fused_ws_bytes(int64_t, int, int, int, int, int) { return 0; }
+constexpr int kChunkTiles = 4;      // Layer1 column tiles per combine chunk (4 x 256 columns)
+constexpr int kCombineTokens = 32;  // tokens per combine work item
+constexpr int kDefaultSpin = 1 << 22;
 
-int fused_default_movers(int64_t, int, int, int, int, int, int, int) { return 0; }
+struct FusedGeom {
+  int mt_max;  // upper bound of M-tiles
+  int nc;      // combine chunks
+};
 
-moe_status_t fused_check(const FusedArgs&, int) { return MOE_ERR_UNSUPPORTED; }
+static FusedGeom fused_geom(int64_t M, int H, int k, int G) {
+  FusedGeom f;
+  const int64_t R = M * k;
+  f.mt_max = (int)((R + kTileRows - 1) / kTileRows) + G;
+  const int nt1 = (H + kL1Cols - 1) / kL1Cols;
+  f.nc = (nt1 + kChunkTiles - 1) / kChunkTiles;
+  return f;
+}
 
-hipError_t launch_fused_layer(const FusedArgs&, hipStream_t) { return hipErrorNotSupported; }
+// flags: l0done[mt_max], chunkdone[nc], queue counters [kXcds + 1]
+constexpr int kQueueWords = kXcds + 1;
+
+size_t fused_ws_bytes(int64_t M, int H, int F, int E, int k, int S) {
+  (void)F;
+  const FusedGeom f = fused_geom(M, H, k, S * E);
+  return (size_t)(f.mt_max + f.nc + kQueueWords) * sizeof(int32_t);
+}
+
+// ---------------------------------------------------------------- flags ---
+__device__ __forceinline__ int ld_flag(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Thread 0 spins until *flag >= target (bounded); the block learns the
+// outcome through LDS.  false: timed out here or elsewhere (status set).
+__device__ bool block_wait(const int32_t* flag, int target, int32_t* status, int limit, int* lds_word) {
+  if (threadIdx.x == 0) {
+    int ok = 1;
+    int polls = 0;
+    while (ld_flag(flag) < target) {
+      if (ld_flag(status) != kStatusOk) {
+        ok = 0;
+        break;
+      }
+      if (++polls > limit) {
+        __hip_atomic_store(status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ok = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    *lds_word = ok;
+  }
+  __syncthreads();
+  const bool ok = *lds_word != 0;
+  __syncthreads();
+  return ok;
+}
+
+// The block's global writes, then one agent-scope release add by thread 0
+// (the workgroup barrier orders the other waves' writes before it).
+__device__ void block_signal(int32_t* flag, int add) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(flag, add, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Next item of a queue counter, shared with the whole block.
+__device__ int block_claim(int32_t* counter, int* lds_word) {
+  if (threadIdx.x == 0) *lds_word = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int v = *lds_word;
+  __syncthreads();
+  return v;
+}
+
+// out[t, columns of chunk c] for tokens [t0, t1) (t1 - t0 <= kCombineTokens).
+// The tokens' row indices and weights are staged in LDS; each thread then
+// owns one 4-column group and walks the tokens 8 at a time, so 8 * k row
+// loads per thread are in flight.
+__device__ void combine_chunk(const FusedArgs& a, int c, int64_t t0, int64_t t1, int* rows_lds, float* w_lds) {
+  const int n0 = c * kChunkTiles * kL1Cols;
+  const int n1 = min(a.H, n0 + kChunkTiles * kL1Cols);
+  const int groups = (n1 - n0) / 4;
+  const int nt = (int)(t1 - t0), k = a.k;
+  for (int i = threadIdx.x; i < nt * k; i += kGemmThreads) {
+    rows_lds[i] = a.f2s[t0 * k + i];
+    w_lds[i] = a.topk_w[t0 * k + i];
+  }
+  __syncthreads();
+  constexpr int U = 8;
+  for (int q = threadIdx.x; q < groups; q += kGemmThreads) {
+    const int64_t n = n0 + 4 * q;
+    for (int i0 = 0; i0 < nt; i0 += U) {
+      float4 o[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = min(i0 + u, nt - 1);
+        o[u] = combine_group(a.y, w_lds + i * k, rows_lds + i * k, k, a.H, n);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (i0 + u < nt) *reinterpret_cast<float4*>(a.out + (t0 + i0 + u) * a.H + n) = o[u];
+    }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kGemmThreads) void fused_layer_kernel(FusedArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[kGemmLdsBytes];
+  __shared__ TileLds tl;
+  __shared__ int lds_word;
+  __shared__ int comb_rows[kCombineTokens * 16];
+  __shared__ float comb_w[kCombineTokens * 16];
+
+  const int MT = build_tile_table(a.offsets, a.G, kTileRows, tl);
+  const int nt0 = (a.F + kL0Cols - 1) / kL0Cols;
+  const int nt1 = (a.H + kL1Cols - 1) / kL1Cols;
+  const int nc = (nt1 + kChunkTiles - 1) / kChunkTiles;
+  int32_t* l0done = a.flags;
+  int32_t* chunkdone = a.flags + a.mt_max;
+  int32_t* mover_q = chunkdone + nc;
+  int32_t* xcd_q = mover_q + 1;
+  const int limit = a.spin_limit > 0 ? a.spin_limit : kDefaultSpin;
+  const int CB = (int)((a.M + kCombineTokens - 1) / kCombineTokens);  // combine items per chunk
+  const bool dedicated = a.n_mover > 0;
+  auto chunk_width = [&](int c) { return min(kChunkTiles, nt1 - c * kChunkTiles); };
+
+  if ((int)blockIdx.x < a.n_mover) {
+    // dedicated combiners: chunk by chunk, token blocks in order
+    for (;;) {
+      const int v = block_claim(mover_q, &lds_word);
+      if (v >= nc * CB) return;
+      const int c = v / CB, tb = v - c * CB;
+      if (!block_wait(chunkdone + c, MT * chunk_width(c), a.status, limit, &lds_word)) return;
+      combine_chunk(a, c, (int64_t)tb * kCombineTokens, min(a.M, (int64_t)(tb + 1) * kCombineTokens), comb_rows,
+                    comb_w);
+    }
+  }
+
+  // the single ordered queue of the other workgroups
+  const int T0 = MT * nt0;
+  int total = T0;
+  for (int c = 0; c < nc; ++c) total += MT * chunk_width(c) + ((dedicated || c == 0) ? 0 : CB);
+  if (!dedicated) total += CB;
+  const int W = gridDim.x - a.n_mover;
+  const int group_cols = W / kXcds > 0 ? W / kXcds : 1;
+  // The queue is dealt to the XCDs in runs of `run` items (run r to queue
+  // r % nq), and the workgroups of one XCD (hardware ids b with the same
+  // b % 8) claim from their queue's counter: the tiles running at once on
+  // an XCD are neighbours in the order and share its L2.  Claims stay in
+  // increasing order per queue, which keeps the no-deadlock argument.
+  const int nq = ((W % kXcds) == 0 && (a.n_mover % kXcds) == 0) ? kXcds : 1;
+  const int run = group_cols;
+  const int q = (nq == 1) ? 0 : (int)(blockIdx.x % kXcds);
+  int32_t* my_q = xcd_q + q;
+  Bf16GemmArgs ga;
+  ga.E = a.E;
+  ga.s2f = a.s2f;
+  ga.topk = a.k;
+  ga.M = a.M;
+  for (;;) {
+    const int i = block_claim(my_q, &lds_word);
+    const int v = (i / run) * (nq * run) + q * run + (i % run);
+    if (v >= total) return;
+    if (v < T0) {
+      const TileCoord c = tile_coord(v, a.G, nt0, kTileRows, group_cols, tl);
+      ga.a = reinterpret_cast<const __bf16*>(a.x);
+      ga.w0 = reinterpret_cast<const __bf16*>(a.w_gate);
+      ga.w1 = reinterpret_cast<const __bf16*>(a.w_up);
+      ga.c = a.hact;
+      ga.K = a.H;
+      ga.N = a.F;
+      bf16_gemm_tile<0, true>(ga, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], c.m0, c.nt, lds);
+      block_signal(l0done + c.mt, 1);
+      continue;
+    }
+    // locate v among the chunk sections
+    int u = v - T0, chunk = 0;
+    bool is_tile = false;
+    int comb_chunk = -1;
+    for (; chunk <= nc; ++chunk) {
+      if (chunk < nc) {
+        const int n = MT * chunk_width(chunk);
+        if (u < n) {
+          is_tile = true;
+          break;
+        }
+        u -= n;
+      }
+      if (!dedicated && chunk >= 1) {
+        if (u < CB) {
+          comb_chunk = chunk - 1;
+          break;
+        }
+        u -= CB;
+      }
+    }
+    if (is_tile) {
+      const TileCoord c = tile_coord(u, a.G, chunk_width(chunk), kTileRows, group_cols, tl);
+      if (!block_wait(l0done + c.mt, nt0, a.status, limit, &lds_word)) return;
+      ga.a = reinterpret_cast<const __bf16*>(a.hact);
+      ga.w0 = reinterpret_cast<const __bf16*>(a.w_down);
+      ga.w1 = nullptr;
+      ga.c = a.y;
+      ga.K = a.F;
+      ga.N = a.H;
+      bf16_gemm_tile<1>(ga, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], c.m0, chunk * kChunkTiles + c.nt, lds);
+      block_signal(chunkdone + chunk, 1);
+    } else if (comb_chunk >= 0) {
+      if (!block_wait(chunkdone + comb_chunk, MT * chunk_width(comb_chunk), a.status, limit, &lds_word)) return;
+      combine_chunk(a, comb_chunk, (int64_t)u * kCombineTokens, min(a.M, (int64_t)(u + 1) * kCombineTokens),
+                    comb_rows, comb_w);
+    }
+  }
+}
+
+// -------------------------------------------------------- split table ---
+// Per-shape plan, profiled on MI355X (256 CUs, one workgroup per CU) with
+// combine_topk_gate_amd/tune_split.py: the number of dedicated combine
+// workgroups of the fused kernel (0: combine items in the shared queue), or
+// -1 where the kernel chain was faster than every fused split.  Shapes not
+// listed run the fused kernel with the combine in the shared queue.
+struct SplitEntry {
+  int64_t M;
+  int H, F, E, k, S, movers;
+};
+static const SplitEntry kSplitTable[] = {
+    {4096, 2048, 1408, 64, 4, 1, -1},
+    {8192, 4096, 14336, 8, 2, 1, -1},
+    {16384, 4096, 6400, 16, 2, 1, -1},
+    {16384, 7168, 4096, 16, 8, 8, -1},
+};
+
+int fused_default_movers(int64_t M, int H, int F, int E, int k, int S, int dtype, int cus) {
+  if (dtype != MOE_DTYPE_BF16) return -1;
+  for (const SplitEntry& s : kSplitTable)
+    if (s.M == M && s.H == H && s.F == F && s.E == E && s.k == k && s.S == S) return s.movers < cus ? s.movers : 0;
+  return 0;
+}
+
+int fused_mt_max(int64_t M, int H, int k, int G) { return fused_geom(M, H, k, G).mt_max; }
+
+// Workgroups of the fused kernel one CU holds at once (LDS and registers).
+static int fused_blocks_per_cu() {
+  static int cached = -1;
+  if (cached < 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fused_layer_kernel, kGemmThreads, 0) != hipSuccess) n = 0;
+    cached = n;
+  }
+  return cached;
+}
+
+moe_status_t fused_check(const FusedArgs& a, int cus) {
+  // every workgroup must be resident at once, or a wait could target work
+  // that has not been scheduled
+  if (a.grid < 1 || a.grid > cus * fused_blocks_per_cu()) return MOE_ERR_UNSUPPORTED;
+  if (a.n_mover < 0 || a.n_mover >= a.grid) return MOE_ERR_INVALID_ARGUMENT;
+  const FusedGeom f = fused_geom(a.M, a.H, a.k, a.G);
+  if (a.mt_max != f.mt_max) return MOE_ERR_INVALID_ARGUMENT;
+  return MOE_OK;
+}
+
+hipError_t launch_fused_layer(const FusedArgs& a, hipStream_t s) {
+  const FusedGeom f = fused_geom(a.M, a.H, a.k, a.G);
+  hipError_t e = launch_fill_i32(a.flags, (int64_t)f.mt_max + f.nc + kQueueWords, 0, s);
+  if (e != hipSuccess) return e;
+  fused_layer_kernel<<<a.grid, kGemmThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
 
 }  // namespace moe

@@ -22,18 +22,19 @@ struct FusedArgs {
   const int32_t* offsets;
   const int32_t* s2f;
   const int32_t* f2s;
-  void* x_perm;
   void* hact;
   float* y;
   float* out;
   int32_t* status;
   int32_t* flags;
+  int mt_max;  // M-tile bound the flag arrays are sized for
   int grid;
   int n_mover;
   int spin_limit;
 };
 
 size_t fused_ws_bytes(int64_t M, int H, int F, int E, int k, int S);
+int fused_mt_max(int64_t M, int H, int k, int G);
 int fused_default_movers(int64_t M, int H, int F, int E, int k, int S, int dtype, int cus);
 moe_status_t fused_check(const FusedArgs& a, int cus);
 hipError_t launch_fused_layer(const FusedArgs& a, hipStream_t s);

@@ -7,12 +7,15 @@
 // weights).  The table is derived on the device from the offsets array, so
 // no host round trip sits between the dispatch and the GEMM.
 //
-// Order: segment by segment; inside a segment, column groups of GN tiles,
-// and inside a group the row tiles fastest.  A persistent workgroup walks
-// virtual slots it*grid + v, and v is chosen so that the workgroups of one
-// XCD (hardware ids w, w+8, ... are dispatched round-robin over the 8 XCDs)
-// own a contiguous run of slots: concurrently running tiles on one XCD then
-// share the expert's weight columns and token rows in that XCD's L2.
+// A segment of n rows has ceil(n / rows) row tiles ("M-tiles"); mt_start[g]
+// is the exclusive prefix of the M-tile counts.  With NT column tiles, the
+// tiles of segment g occupy [mt_start[g] * NT, mt_start[g+1] * NT) of the
+// queue.  Inside a segment: column groups of gn tiles, and inside a group
+// the row tiles fastest.  A persistent workgroup walks virtual slots
+// it*grid + v, and v is chosen so that the workgroups of one XCD (hardware
+// ids w, w+8, ... are dispatched round-robin over the 8 XCDs) own a
+// contiguous run of slots: concurrently running tiles on one XCD then share
+// the expert's weight columns and token rows in that XCD's L2.
 #pragma once
 
 #include "common.hpp"
@@ -22,80 +25,85 @@ namespace moe {
 constexpr int kMaxTileSegs = 1024;
 constexpr int kXcds = 8;
 
-struct TileTable {
-  int G;
-  int NT;     // column tiles per segment
-  int rows;   // row tile height
-  int total;  // total tiles
+struct TileLds {
+  int seg_start[kMaxTileSegs + 1];
+  int seg_rows[kMaxTileSegs + 1];
+  int mt_start[kMaxTileSegs + 1];
+  int scratch[256];
 };
 
-// Fills LDS arrays (each sized kMaxTileSegs + 1): seg_start[g] (first row),
-// seg_rows[g], tile_start[g] (exclusive prefix of tiles); returns the total.
-// All threads of the block must call it.
-__device__ inline int build_tile_table(const int32_t* __restrict__ offsets, int G, int NT, int rows,
-                                       int* seg_start, int* seg_rows, int* tile_start, int* scratch) {
+// Fills seg_start, seg_rows and mt_start from offsets; returns the number of
+// M-tiles.  All threads of the block (<= 256) must call it.
+__device__ inline int build_tile_table(const int32_t* __restrict__ offsets, int G, int rows, TileLds& t) {
   const int nthr = blockDim.x;
-  // per-thread serial prefix over a contiguous run of segments, then a scan of run totals
   const int per = (G + nthr - 1) / nthr;
   const int g0 = threadIdx.x * per;
   int run = 0;
   for (int g = g0; g < g0 + per && g < G; ++g) {
     const int a = offsets[g], b = offsets[g + 1];
-    seg_start[g] = a;
-    seg_rows[g] = b - a;
-    run += ((b - a + rows - 1) / rows) * NT;
+    t.seg_start[g] = a;
+    t.seg_rows[g] = b - a;
+    run += (b - a + rows - 1) / rows;
   }
-  scratch[threadIdx.x] = run;
+  t.scratch[threadIdx.x] = run;
   __syncthreads();
   for (int off = 1; off < nthr; off <<= 1) {
-    const int v = (threadIdx.x >= (unsigned)off) ? scratch[threadIdx.x - off] : 0;
+    const int v = (threadIdx.x >= (unsigned)off) ? t.scratch[threadIdx.x - off] : 0;
     __syncthreads();
-    scratch[threadIdx.x] += v;
+    t.scratch[threadIdx.x] += v;
     __syncthreads();
   }
-  int acc = scratch[threadIdx.x] - run;
+  int acc = t.scratch[threadIdx.x] - run;
   for (int g = g0; g < g0 + per && g < G; ++g) {
-    tile_start[g] = acc;
-    acc += ((seg_rows[g] + rows - 1) / rows) * NT;
+    t.mt_start[g] = acc;
+    acc += (t.seg_rows[g] + rows - 1) / rows;
   }
-  const int total = scratch[nthr - 1];
-  if (threadIdx.x == 0) tile_start[G] = total;
+  const int total = t.scratch[nthr - 1];
+  if (threadIdx.x == 0) t.mt_start[G] = total;
   __syncthreads();
   return total;
 }
 
-struct TileCoord {
-  int g;       // segment
-  int m0;      // first row of the tile inside the segment
-  int nt;      // column tile index
-};
-
-// Map a tile index to (segment, row tile, column tile).
-__device__ inline TileCoord tile_coord(int v, int G, int NT, int rows, int group_cols, const int* seg_rows,
-                                       const int* tile_start) {
-  int lo = 0, hi = G - 1;  // last g with tile_start[g] <= v
+// Last segment g with mt_start[g] * mult <= v (v below the total).
+__device__ inline int find_segment(int v, int G, int mult, const int* mt_start) {
+  int lo = 0, hi = G - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (tile_start[mid] <= v) lo = mid; else hi = mid - 1;
+    if (mt_start[mid] * mult <= v) lo = mid; else hi = mid - 1;
   }
-  const int g = lo;
-  const int l = v - tile_start[g];
-  const int mt = (seg_rows[g] + rows - 1) / rows;
+  return lo;
+}
+
+struct TileCoord {
+  int g;   // segment
+  int m0;  // first row of the tile inside the segment
+  int nt;  // column tile index (relative to the column range the queue covers)
+  int mt;  // global M-tile index
+};
+
+// Tile v of a queue over NT column tiles (per segment mt_g * NT tiles).
+__device__ inline TileCoord tile_coord(int v, int G, int NT, int rows, int group_cols, const TileLds& t) {
+  const int g = find_segment(v, G, NT, t.mt_start);
+  const int l = v - t.mt_start[g] * NT;
+  const int mt = t.mt_start[g + 1] - t.mt_start[g];
   int gn = group_cols / (mt > 0 ? mt : 1);
   if (gn < 1) gn = 1;
   const int span = mt * gn;
   const int grp = l / span, rem = l - grp * span;
   TileCoord c;
   c.g = g;
-  c.m0 = (rem % mt) * rows;
+  const int mi = rem % mt;
+  c.m0 = mi * rows;
   c.nt = grp * gn + rem / mt;
+  c.mt = t.mt_start[g] + mi;
   return c;
 }
 
-// Virtual slot of this workgroup: the workgroups of one XCD get a contiguous run.
-__device__ __forceinline__ int xcd_slot(int wg, int grid) {
-  if (grid % kXcds != 0) return wg;
-  const int per = grid / kXcds;
+// Virtual slot of workgroup `wg` among `n` workgroups: the workgroups of one
+// XCD get a contiguous run of slots.
+__device__ __forceinline__ int xcd_slot(int wg, int n) {
+  if (n % kXcds != 0) return wg;
+  const int per = n / kXcds;
   return (wg % kXcds) * per + wg / kXcds;
 }
 

@@ -1,0 +1,88 @@
+"""Profile the fused layer's split on this GPU and print the table entries.
+
+    python -m combine_topk_gate_amd.tune_split [--configs qwen2,mixtral,...] [--reps 10]
+
+For each workload it times moe_layer as the kernel chain and as the fused
+kernel with every candidate number of dedicated combine workgroups
+(0 = combine items in the shared queue), and prints one JSON line per
+workload plus the C++ table rows (the split table in csrc/layer.hip) for the
+fastest fused split.  The split is picked ahead of time and looked up at
+run time, as COMET does with its profiled per-shape metadata (paper review
+§4.2.2).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--configs", default="qwen2,mixtral,phi35,epshare")
+    ap.add_argument("--movers", default="0,2,4,8,16,32")
+    ap.add_argument("--reps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    args = ap.parse_args()
+
+    import torch
+
+    import combine_topk_gate_amd as moe
+    import moe_synth
+
+    def up(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to("cuda:0").view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+    rows = []
+    for name in args.configs.split(","):
+        cfg = moe_synth.config(name)
+        d = moe_synth.make_inputs(cfg)
+        g = {k: up(v) for k, v in d.items()}
+        del d
+        p = moe.problem(cfg.M, cfg.H, cfg.F, cfg.E, cfg.k, cfg.S, cfg.dtype)
+        ws = torch.empty(moe.moe_workspace_bytes(p, moe.MOE_OP_LAYER), dtype=torch.uint8, device="cuda:0")
+        out = torch.empty((cfg.M, cfg.H), dtype=torch.float32, device="cuda:0")
+
+        def run(**opts):
+            moe.moe_layer(p, g["x"], g["logits"], g.get("src_block"), g["w_gate"], g["w_up"], g["w_down"], out,
+                          ws, **opts)
+
+        def timeit(**opts):
+            for _ in range(args.warmup):
+                run(**opts)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.reps):
+                run(**opts)
+            e1.record()
+            torch.cuda.synchronize()
+            assert moe.moe_debug_device_status(p, ws) == moe.MOE_OK
+            return e0.elapsed_time(e1) / args.reps * 1e3
+
+        res = {"config": name, "chain_us": timeit(fused=0)}
+        for m in (int(v) for v in args.movers.split(",")):
+            res[f"fused_m{m}_us"] = timeit(fused=1, n_mover=m)
+        best = min((v, k) for k, v in res.items() if k.startswith("fused_"))
+        res["best"] = best[1]
+        print(json.dumps(res), flush=True)
+        m = int(best[1].split("_m")[1].split("_")[0])
+        rows.append(f"    {{{cfg.M}, {cfg.H}, {cfg.F}, {cfg.E}, {cfg.k}, {cfg.S}, {m}}},")
+        del g, ws, out
+        torch.cuda.empty_cache()
+    print("\n".join(rows))
+
+
+if __name__ == "__main__":
+    main()

@@ -8,8 +8,9 @@
  *   grouped   Layer0: gate/up products + SwiGLU; Layer1: down product,
  *   GEMM      both as one grouped GEMM over all experts
  *   combine   top-k weighted reduction of each token's expert outputs
- *   layer     all of the above, with the dispatch copy and the combine done
- *             by dedicated workgroups beside the matrix-core workgroups
+ *   layer     all of the above in one persistent kernel: one ordered work
+ *             queue of Layer0 tiles, Layer1 tiles and combine items, with
+ *             ready counters between them
  *
  * Sources (cited by page and section):
  *   [COMET]  "COMET: Fine-grained Computation-communication Overlapping for
@@ -167,7 +168,8 @@ typedef struct {
 /* Schedule options of the fused layer (NULL = defaults).  Results do not
  * depend on them: every output element is computed in a fixed order. */
 typedef struct {
-  int32_t n_mover;     /* workgroups that copy and combine; <0: from the profiled split table */
+  int32_t n_mover;     /* dedicated combine workgroups; 0: combine items share the work queue;
+                          <0: the profiled split table's plan (which may be the chain) */
   int32_t grid;        /* total persistent workgroups; <=0: every CU, one each */
   int32_t fused;       /* 0: run the unfused kernel chain instead of the fused kernel */
   int32_t spin_limit;  /* >0: bound on each device wait (polls); 0: default bound */
@@ -175,27 +177,37 @@ typedef struct {
 
 /*
  * The whole layer ([COMET] §4.2.1 thread-block specialisation, §4.2.2
- * adaptive allocation; [PTO] MegaMoE seven-stage fusion): route, dispatch,
- * Layer0, Layer1 and combine.  The fused kernel runs n_mover "mover"
- * workgroups that gather token rows tile by tile and later combine each
- * column chunk as soon as its Layer1 tiles are done, beside matrix-core
- * workgroups that take Layer0 then Layer1 tiles from one ordered queue;
- * per-tile counters in the workspace act as ready flags.  The output equals,
- * bit for bit, the unfused chain moe_route -> moe_dispatch ->
- * moe_grouped_gemm(0) -> moe_grouped_gemm(1) -> moe_combine.
+ * adaptive allocation, §4.1.1-§4.1.2 shared-tensor decomposition and
+ * column-wise Layer1; [PTO] MegaMoE seven-stage fusion, ready counters,
+ * dynamic core grouping): route, dispatch bookkeeping, then one persistent
+ * kernel (bf16 layers) whose workgroups take, from one ordered queue,
+ * Layer0 tiles (token rows read straight from x through sorted_to_flat),
+ * Layer1 tiles column chunk by column chunk (each once its row tile's
+ * Layer0 tiles are done), and combine items (a column chunk of a block of
+ * tokens, once that chunk's Layer1 tiles are done) -- either on n_mover
+ * dedicated workgroups or in the shared queue.  Counters in the workspace
+ * are the ready flags.  f32 layers, and opts->fused == 0, run the kernel
+ * chain moe_route -> moe_dispatch -> moe_grouped_gemm(0) ->
+ * moe_grouped_gemm(1) -> moe_combine instead; both paths give the same bits.
  *   x [M,H] dtype; logits [M,E] f32; src_block [M] int32 or NULL (S = 1);
  *   w_gate, w_up [E,F,H]; w_down [E,H,F]; out [M,H] f32.
- * If a bounded device wait runs out, the kernel stops early and records
- * MOE_ERR_DEVICE_TIMEOUT in the workspace; read it with
- * moe_debug_device_status.
+ *   aux: the fused path writes X_perm only if aux->x_perm is given.
+ * The fused kernel needs its whole grid resident (one workgroup per CU):
+ * opts->grid above that returns MOE_ERR_UNSUPPORTED; n_mover >= grid returns
+ * MOE_ERR_INVALID_ARGUMENT.  If a bounded device wait runs out, the kernel
+ * stops early and records MOE_ERR_DEVICE_TIMEOUT in the workspace; read it
+ * with moe_debug_device_status.
  */
 moe_status_t moe_layer(const moe_problem_t* p, const void* x, const float* logits, const int32_t* src_block,
                        const void* w_gate, const void* w_up, const void* w_down, float* out,
                        const moe_layer_aux_t* aux, const moe_layer_opts_t* opts, void* ws, size_t ws_bytes,
                        void* stream);
 
-/* Mover workgroups the profiled split table picks for this problem (the
- * value moe_layer uses when opts->n_mover < 0), or -1 for an invalid problem. */
+/* The plan the profiled split table picks for this problem (what moe_layer
+ * does when opts->n_mover < 0): the number of dedicated combine workgroups
+ * of the fused kernel (0: the combine shares the work queue), or -1 when the
+ * layer runs as the kernel chain (f32 layers, and shapes where profiling
+ * found the chain faster) or the problem is invalid. */
 int32_t moe_layer_default_movers(const moe_problem_t* p);
 
 /* Synchronises `stream` and returns the device status the last moe_layer

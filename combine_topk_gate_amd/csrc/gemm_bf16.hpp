@@ -23,8 +23,10 @@
 //    double-buffered ("Double-buffer pipeline": the next K slice loads while
 //    the matrix cores work on the current one), one barrier per K step.
 //  * LDS rows are 128 B; 16-byte chunk c of row r is stored at slot
-//    c ^ (r & 7), so the 8 lanes of each ds_read_b128 phase hit 8 different
-//    bank groups.
+//    c ^ swz(r), swz(r) = (r & 7) ^ ((r >> 3) & 1).  A ds_read_b128 of 32
+//    consecutive rows then hits distinct 16-byte bank groups in every group
+//    of 16 lanes (64 banks: rows r and r+1 share a 256-byte bank line) and
+//    in every group of 8 lanes (32 banks).
 #pragma once
 
 #include "common.hpp"
@@ -115,7 +117,7 @@ __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int
 #pragma unroll
     for (int i = 0; i < 8; ++i) xvoff[i] = voff0 + (uint32_t)i * vstep;
   }
-  const uint32_t st_off = (uint32_t)lr * 128u + ((uint32_t)(lc ^ (lr & 7)) << 4);
+  const uint32_t st_off = (uint32_t)lr * 128u + ((uint32_t)(lc ^ (lr & 7) ^ ((lr >> 3) & 1)) << 4);
 
   // Global loads in 4 parts (one per k16 sub-step of the MFMA loop); part q
   // covers the thread's rows lr + 32 i for i in {2q, 2q+1}, weights and tokens.
@@ -153,7 +155,7 @@ __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int
   const uint32_t xrow_off = (uint32_t)(kOperandBytes + (wm * 128 + lrow) * 128);
   uint32_t kswz[4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) kswz[ks] = (uint32_t)(((2 * ks + lk) ^ (lrow & 7)) << 4);
+  for (int ks = 0; ks < 4; ++ks) kswz[ks] = (uint32_t)(((2 * ks + lk) ^ (lrow & 7) ^ ((lrow >> 3) & 1)) << 4);
 
   // two register sets of fragments: sub-step ks uses set ks & 1 while the
   // reads for ks + 1 fill the other set

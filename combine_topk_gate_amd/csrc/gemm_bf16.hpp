@@ -9,15 +9,18 @@
 // with every product accumulated in f32 by the matrix cores, k increasing.
 //
 // Design for CDNA4:
-//  * The tile is 256 weight rows x 256 token rows, K stepped by 64.  The
-//    weight rows are the MFMA "A" operand and the token rows the "B"
-//    operand, so each lane's accumulators hold 4 consecutive output columns
-//    of one token row: the epilogue stores 8 B (bf16) / 16 B (f32) vectors.
+//  * The tile is 256 weight rows x TM token rows (TM = 256, or 128 for a
+//    half tile), K stepped by 64.  The weight rows are the MFMA "A" operand
+//    and the token rows the "B" operand, so each lane's accumulators hold 4
+//    consecutive output columns of one token row: the epilogue stores 8 B
+//    (bf16) / 16 B (f32) vectors.  A half tile computes every element the
+//    same way as a full tile (same k order), so which height covers a row
+//    never changes a bit of the result.
 //  * Layer0's 256 weight rows are 128 gate rows and the 128 up rows of the
 //    same columns, so a lane holds gate and up for the same (r, f) and the
 //    SwiGLU runs in registers before the single bf16 store.
-//  * 4 waves in a 2 x 2 arrangement, 128 x 128 per wave = 4 x 4 blocks of
-//    v_mfma_f32_32x32x16_bf16 (256 f32 accumulators per lane).
+//  * 4 waves in a 2 x 2 arrangement, 128 x TM/2 per wave = 4 x TM/64 blocks
+//    of v_mfma_f32_32x32x16_bf16 (up to 256 f32 accumulators per lane).
 //  * Operands stream HBM -> VGPR (buffer loads whose range check returns 0
 //    past the segment end, so ragged row tiles need no masking) -> LDS,
 //    double-buffered ("Double-buffer pipeline": the next K slice loads while
@@ -67,9 +70,13 @@ __device__ __forceinline__ i32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-template <int LAYER, bool GATHER = false>
+template <int LAYER, bool GATHER = false, int TM = kTileRows>
 __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int seg_start, int seg_rows, int m0,
                                                int nt, char* __restrict__ lds) {
+  static_assert(TM == 256 || TM == 128, "token tile height");
+  constexpr int NJ = TM / 64;      // token fragments per wave
+  constexpr int XI = TM / 32;      // token-row loads per thread per K step
+  constexpr int XQ = XI / 4;       // ... per sub-step
   // tile coordinates come from LDS; make them provably wave-uniform so the
   // buffer descriptors live in SGPRs (no per-lane descriptor loops)
   g = uniform(g);
@@ -98,16 +105,16 @@ __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int
     rw0 = make_rsrc(p.w0 + ebase + (int64_t)col0 * K, (uint32_t)ncols * row_bytes);
     rw1 = rw0;
   }
-  const int trows = min(seg_rows - m0, kTileRows);
+  const int trows = min(seg_rows - m0, TM);
   const uint32_t voff0 = (uint32_t)lr * row_bytes + (uint32_t)lc * 16u;
   const uint32_t vstep = 32u * row_bytes;
   __amdgpu_buffer_rsrc_t rx;
-  uint32_t xvoff[8];
+  uint32_t xvoff[XI];
   if (GATHER) {
     // token rows of x; rows past the segment end read zeros (offset past the range)
     rx = make_rsrc(p.a, (uint32_t)(p.M * (int64_t)row_bytes));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < XI; ++i) {
       const int r = lr + 32 * i;
       xvoff[i] = 0x80000000u;
       if (r < trows) xvoff[i] = (uint32_t)(p.s2f[seg_start + m0 + r] / p.topk) * row_bytes + (uint32_t)lc * 16u;
@@ -115,13 +122,14 @@ __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int
   } else {
     rx = make_rsrc(p.a + (int64_t)(seg_start + m0) * K, (uint32_t)trows * row_bytes);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) xvoff[i] = voff0 + (uint32_t)i * vstep;
+    for (int i = 0; i < XI; ++i) xvoff[i] = voff0 + (uint32_t)i * vstep;
   }
   const uint32_t st_off = (uint32_t)lr * 128u + ((uint32_t)(lc ^ (lr & 7) ^ ((lr >> 3) & 1)) << 4);
 
   // Global loads in 4 parts (one per k16 sub-step of the MFMA loop); part q
-  // covers the thread's rows lr + 32 i for i in {2q, 2q+1}, weights and tokens.
-  i32x4_t wreg[8], xreg[8];
+  // covers the thread's weight rows lr + 32 i, i in {2q, 2q+1}, and token
+  // rows lr + 32 i, i in [q XQ, (q+1) XQ).
+  i32x4_t wreg[8], xreg[XI];
   auto gload_part = [&](int kt, int q) {
     const uint32_t soff = (uint32_t)kt * (kBK * 2);
 #pragma unroll
@@ -130,17 +138,17 @@ __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int
         wreg[i] = buf_load16(i < 4 ? rw0 : rw1, voff0 + (uint32_t)(i & 3) * vstep, soff);
       else
         wreg[i] = buf_load16(rw0, voff0 + (uint32_t)i * vstep, soff);
-      xreg[i] = buf_load16(rx, xvoff[i], soff);
     }
+#pragma unroll
+    for (int i = q * XQ; i < (q + 1) * XQ; ++i) xreg[i] = buf_load16(rx, xvoff[i], soff);
   };
   auto lstore_part = [&](int stage, int q) {
     char* wdst = lds + stage * kStageBytes + st_off;
     char* xdst = wdst + kOperandBytes;
 #pragma unroll
-    for (int i = 2 * q; i < 2 * q + 2; ++i) {
-      *reinterpret_cast<i32x4_t*>(wdst + i * 4096) = wreg[i];
-      *reinterpret_cast<i32x4_t*>(xdst + i * 4096) = xreg[i];
-    }
+    for (int i = 2 * q; i < 2 * q + 2; ++i) *reinterpret_cast<i32x4_t*>(wdst + i * 4096) = wreg[i];
+#pragma unroll
+    for (int i = q * XQ; i < (q + 1) * XQ; ++i) *reinterpret_cast<i32x4_t*>(xdst + i * 4096) = xreg[i];
   };
 
   // ---- fragment addressing
@@ -152,37 +160,37 @@ __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int
                                : wn * 128 + mi * 32 + lrow;
     wrow_off[mi] = (uint32_t)r * 128u;
   }
-  const uint32_t xrow_off = (uint32_t)(kOperandBytes + (wm * 128 + lrow) * 128);
+  const uint32_t xrow_off = (uint32_t)(kOperandBytes + (wm * (TM / 2) + lrow) * 128);
   uint32_t kswz[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) kswz[ks] = (uint32_t)(((2 * ks + lk) ^ (lrow & 7) ^ ((lrow >> 3) & 1)) << 4);
 
   // two register sets of fragments: sub-step ks uses set ks & 1 while the
   // reads for ks + 1 fill the other set
-  bf16x8_t fa[2][4], fb[2][4];
+  bf16x8_t fa[2][4], fb[2][NJ];
   auto read_frags = [&](int set, int stage, int ks) {
     const char* base = lds + stage * kStageBytes;
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
       fa[set][mi] = *reinterpret_cast<const bf16x8_t*>(base + wrow_off[mi] + kswz[ks]);
 #pragma unroll
-    for (int nj = 0; nj < 4; ++nj)
+    for (int nj = 0; nj < NJ; ++nj)
       fb[set][nj] = *reinterpret_cast<const bf16x8_t*>(base + xrow_off + nj * 4096 + kswz[ks]);
   };
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][NJ];
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int nj = 0; nj < 4; ++nj)
+    for (int nj = 0; nj < NJ; ++nj)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mi][nj][v] = 0.0f;
 
-  auto mfma_step = [&](int set) {
+  auto mfma_rows = [&](int set, int mi0, int mi1) {
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int mi = mi0; mi < mi1; ++mi)
 #pragma unroll
-      for (int nj = 0; nj < 4; ++nj)
+      for (int nj = 0; nj < NJ; ++nj)
         acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][mi], fb[set][nj], acc[mi][nj], 0, 0, 0);
   };
 
@@ -202,19 +210,20 @@ __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int
   // (a) the registers holding stage kt+1 drain into the other buffer and
   // (b) the registers refill with stage kt+2 from HBM/L2, a quarter per
   // sub-step, so neither the LDS writes nor the loads sit in one burst.
-  // The barrier comes before the last sub-step's MFMAs: the reads of the
-  // next stage's first fragments are then in flight while those MFMAs run.
-  // The last iteration's stores, loads and reads run too (on a clamped, valid
-  // slice into the idle buffer) so the loop body has no branches; every LDS
-  // access of the tile precedes its last barrier, so the next tile's
-  // prologue may overwrite either buffer.
+  // The barrier comes before the last sub-step's second half of MFMAs: the
+  // reads of the next stage's first fragments are then in flight while
+  // those MFMAs run.  The last iteration's stores, loads and reads run too
+  // (on a clamped, valid slice into the idle buffer) so the loop body has
+  // no branches; every LDS access of the tile precedes its last barrier, so
+  // the next tile's prologue may overwrite either buffer.
   //
   // One wave per SIMD cannot hide an LDS read behind another wave, so the
-  // order inside each k16 sub-step is pinned with scheduling groups: the 16
-  // MFMAs of sub-step ks alternate with the 8 fragment reads of ks + 1, the
-  // 4 LDS stores of stage kt+1 and the 4 loads of stage kt+2.  In the last
-  // sub-step the barrier sits after 8 of the 16 MFMAs, and the first reads
-  // of stage kt+1 go out between the remaining 8.
+  // order inside each k16 sub-step is pinned with scheduling groups: the
+  // MFMAs of sub-step ks alternate with the fragment reads of ks + 1, the LDS
+  // stores of stage kt+1 and the loads of stage kt+2.
+  constexpr int NR = 4 + NJ;        // fragment reads per sub-step
+  constexpr int NW = 2 + XQ;        // LDS stores (and loads) per sub-step
+  constexpr int NM = 4 * NJ;        // MFMAs per sub-step
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1, nxt = cur ^ 1;
     const int kload = (kt + 2 < nk) ? kt + 2 : nk - 1;
@@ -223,56 +232,58 @@ __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int
       read_frags((ks + 1) & 1, cur, ks + 1);
       lstore_part(nxt, ks);
       gload_part(kload, ks);
-      mfma_step(ks & 1);
+      mfma_rows(ks & 1, 0, 4);
+      if constexpr (TM == 256) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-      }
+        for (int i = 0; i < NR; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
-      }
+        for (int i = 0; i < NW; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+        }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+        for (int i = 0; i < NW; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+        }
+      } else {
+        // 8 MFMAs for 6 reads, 3 stores, 3 loads
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x200, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 3, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     // sub-step 3: first half of the MFMAs with the last stores and loads
     lstore_part(nxt, 3);
     gload_part(kload, 3);
+    mfma_rows(1, 0, 2);
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-      for (int nj = 0; nj < 4; ++nj)
-        acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][mi], fb[1][nj], acc[mi][nj], 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < NM / 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+      __builtin_amdgcn_sched_group_barrier(0x220, 1, 0);  // DS write or VMEM read
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
-    }
+    if constexpr (2 * NW > NM / 2) __builtin_amdgcn_sched_group_barrier(0x220, 2 * NW - NM / 2, 0);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
     read_frags(0, nxt, 0);
+    mfma_rows(1, 2, 4);
 #pragma unroll
-    for (int mi = 2; mi < 4; ++mi)
-#pragma unroll
-      for (int nj = 0; nj < 4; ++nj)
-        acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1][mi], fb[1][nj], acc[mi][nj], 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < NM / 2; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
     }
+    if constexpr (NR > NM / 2) __builtin_amdgcn_sched_group_barrier(0x100, NR - NM / 2, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -280,8 +291,8 @@ __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int
   if (LAYER == 0) {
     __bf16* hact = reinterpret_cast<__bf16*>(p.c);
 #pragma unroll
-    for (int nj = 0; nj < 4; ++nj) {
-      const int trow = m0 + wm * 128 + nj * 32 + lrow;
+    for (int nj = 0; nj < NJ; ++nj) {
+      const int trow = m0 + wm * (TM / 2) + nj * 32 + lrow;
       if (trow >= seg_rows) continue;
       __bf16* dst = hact + (int64_t)(seg_start + trow) * N;
 #pragma unroll
@@ -303,8 +314,8 @@ __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int
   } else {
     float* y = reinterpret_cast<float*>(p.c);
 #pragma unroll
-    for (int nj = 0; nj < 4; ++nj) {
-      const int trow = m0 + wm * 128 + nj * 32 + lrow;
+    for (int nj = 0; nj < NJ; ++nj) {
+      const int trow = m0 + wm * (TM / 2) + nj * 32 + lrow;
       if (trow >= seg_rows) continue;
       float* dst = y + (int64_t)(seg_start + trow) * N;
 #pragma unroll

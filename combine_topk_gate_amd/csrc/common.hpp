@@ -33,6 +33,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
 
+// silu(g) * u for the bf16 layers' epilogue, with the hardware base-2
+// exponential and reciprocal (about 1 ulp each): silu(g) = g / (1 + e^-g)
+// = g * rcp(1 + 2^(-g log2 e)).  Its error (~1e-7 relative) is far below
+// the bf16 rounding of the activation that follows; for g -> -inf the
+// exponential saturates to +inf and the reciprocal to 0, the exact limit.
+__device__ __forceinline__ float silu_mul_fast(float g, float u) {
+  const float e = __builtin_amdgcn_exp2f(g * -1.44269504088896341f);
+  return (g * u) * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
 // Top-k weighted reduction of one 4-wide column group, shared by the
 // stand-alone combine and the fused layer so both give identical bits.
 __device__ __forceinline__ float4 combine_group(const float* __restrict__ y, const float* __restrict__ w,

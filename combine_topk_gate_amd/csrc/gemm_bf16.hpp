@@ -5,6 +5,7 @@
 // COMET paper review §3.2: Layer0 = gate/up, Layer1 = down; PTO MoE
 // article: GMM1 -> SwiGLU -> GMM2):
 //   layer 0: Hact[r, f] = bf16( silu(X[r]·Wg[e,f]) * (X[r]·Wu[e,f]) )
+//            (silu with the hardware exp2 / reciprocal, see silu_mul_fast)
 //   layer 1: Y[r, n]    = Hact[r]·Wd[e,n]            (f32)
 // with every product accumulated in f32 by the matrix cores, k increasing.
 //
@@ -305,7 +306,7 @@ __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const float gt = acc[mi][nj][4 * q + v], up = acc[mi + 2][nj][4 * q + v];
-            h[v] = (__bf16)(silu_f32(gt) * up);
+            h[v] = (__bf16)silu_mul_fast(gt, up);
           }
           *reinterpret_cast<bf16x4_t*>(dst + f) = h;
         }

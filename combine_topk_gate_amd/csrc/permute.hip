@@ -48,35 +48,62 @@ __global__ __launch_bounds__(kPermThreads) void seg_count_kernel(const int32_t* 
   for (int g = threadIdx.x; g < G; g += kPermThreads) block_hist[(int64_t)blockIdx.x * G + g] = hist[g];
 }
 
+// Column-wise exclusive scan of block_hist [blocks][G] (in place), the
+// per-segment totals (counts) and their exclusive scan (offsets).  Thread
+// layout: P = 1024 / G' threads per segment (G' = G rounded up to a power of
+// two), each owning a contiguous slice of the blocks, so every thread issues
+// independent loads and the chain of dependent adds stays short.
 __global__ __launch_bounds__(kMaxSegments) void seg_scan_kernel(int G, int blocks, int64_t R,
                                                                 int32_t* __restrict__ block_hist,
                                                                 int32_t* __restrict__ counts,
                                                                 int32_t* __restrict__ offsets) {
+  __shared__ int part[kMaxSegments];
   __shared__ int s[kMaxSegments];
-  const int g = threadIdx.x;
-  int total = 0;
-  if (g < G) {
-    for (int b = 0; b < blocks; ++b) {
-      const int c = block_hist[(int64_t)b * G + g];
-      block_hist[(int64_t)b * G + g] = total;
-      total += c;
-    }
-    counts[g] = total;
-  }
-  s[g] = (g < G) ? total : 0;
+  __shared__ int tot[kMaxSegments];
+  int gp = 1;
+  while (gp < G) gp <<= 1;
+  const int P = kMaxSegments / gp;  // threads per segment
+  const int g = threadIdx.x % gp, p = threadIdx.x / gp;
+  const int L = (blocks + P - 1) / P;
+  const int b0 = p * L, b1 = min(blocks, b0 + L);
+  int sum = 0;
+  if (g < G)
+    for (int b = b0; b < b1; ++b) sum += block_hist[(int64_t)b * G + g];
+  part[threadIdx.x] = sum;
   __syncthreads();
-  for (int off = 1; off < kMaxSegments; off <<= 1) {
-    const int v = (g >= off) ? s[g - off] : 0;
+  // exclusive prefix over the P slices of each segment, and the segment total
+  if (threadIdx.x < gp) {
+    int run = 0;
+    for (int q = 0; q < P; ++q) {
+      const int v = part[q * gp + threadIdx.x];
+      part[q * gp + threadIdx.x] = run;
+      run += v;
+    }
+    s[threadIdx.x] = (threadIdx.x < G) ? run : 0;
+  }
+  __syncthreads();
+  const int total = (threadIdx.x < gp) ? s[threadIdx.x] : 0;
+  if (threadIdx.x < gp) tot[threadIdx.x] = total;
+  if (threadIdx.x < G) counts[threadIdx.x] = total;
+  // exclusive scan of the totals over segments
+  for (int off = 1; off < gp; off <<= 1) {
+    const int v = (threadIdx.x < gp && threadIdx.x >= (unsigned)off) ? s[threadIdx.x - off] : 0;
     __syncthreads();
-    s[g] += v;
+    if (threadIdx.x < gp) s[threadIdx.x] += v;
     __syncthreads();
   }
+  if (threadIdx.x < G) offsets[threadIdx.x] = s[threadIdx.x] - total;
+  if (threadIdx.x == 0) offsets[G] = (int)R;
+  __syncthreads();
+  // block_hist[b][g] <- offsets[g] + pairs of segment g in blocks before b
   if (g < G) {
-    const int start = s[g] - total;  // exclusive prefix
-    offsets[g] = start;
-    for (int b = 0; b < blocks; ++b) block_hist[(int64_t)b * G + g] += start;
+    int run = s[g] - tot[g] + part[threadIdx.x];  // offsets[g] + blocks before this slice
+    for (int b = b0; b < b1; ++b) {
+      const int v = block_hist[(int64_t)b * G + g];
+      block_hist[(int64_t)b * G + g] = run;
+      run += v;
+    }
   }
-  if (g == 0) offsets[G] = (int)R;
 }
 
 __global__ __launch_bounds__(kPermThreads) void seg_rank_kernel(const int32_t* __restrict__ topk_idx,
@@ -130,7 +157,9 @@ PermutePlan permute_plan(int64_t M, int k, int G) {
   PermutePlan pl;
   pl.R = M * k;
   pl.G = G;
-  int64_t chunk = 4096;
+  // small chunks: many blocks rank in parallel (the ranking of one chunk is
+  // sequential in steps of 256 pairs)
+  int64_t chunk = 512;
   const int64_t want = (pl.R + 1023) / 1024;  // at most 1024 chunks
   if (want > chunk) chunk = ((want + kPermThreads - 1) / kPermThreads) * kPermThreads;
   pl.chunk = (int)chunk;
@@ -156,29 +185,38 @@ hipError_t launch_permute(const PermutePlan& pl, const int32_t* topk_idx, const 
 
 // ------------------------------------------------------------ dispatch ---
 // Each token row is read once and written to its k sorted positions,
-// 16 bytes per lane; a block walks whole rows so the writes of one row are
-// contiguous.
+// 16 bytes per lane; a block walks whole rows (two at a time, so each lane
+// has several loads in flight) and the writes of one row are contiguous.
+// X_perm is written with non-temporal stores: it is consumed by the next
+// kernel from HBM, so keeping it out of the caches leaves them to the reads.
 constexpr int kCopyThreads = 256;
-constexpr int kCopyUnroll = 4;
+constexpr int kCopyRows = 2;
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(kCopyThreads) void dispatch_copy_kernel(const uint4* __restrict__ x, int64_t M, int C,
-                                                                     int k, const int32_t* __restrict__ f2s,
-                                                                     uint4* __restrict__ xp) {
-  for (int64_t t = blockIdx.x; t < M; t += gridDim.x) {
-    const uint4* src = x + t * C;
-    for (int c0 = threadIdx.x; c0 < C; c0 += kCopyThreads * kCopyUnroll) {
-      uint4 v[kCopyUnroll];
+__global__ __launch_bounds__(kCopyThreads) void dispatch_copy_kernel(const u32x4_t* __restrict__ x, int64_t M,
+                                                                     int C, int k, const int32_t* __restrict__ f2s,
+                                                                     u32x4_t* __restrict__ xp) {
+  for (int64_t t0 = (int64_t)blockIdx.x * kCopyRows; t0 < M; t0 += (int64_t)gridDim.x * kCopyRows) {
+    const int nr = (M - t0) < kCopyRows ? (int)(M - t0) : kCopyRows;
+    for (int c0 = threadIdx.x; c0 < C; c0 += kCopyThreads * 2) {
+      u32x4_t v[kCopyRows][2];
 #pragma unroll
-      for (int u = 0; u < kCopyUnroll; ++u) {
-        const int c = c0 + u * kCopyThreads;
-        if (c < C) v[u] = src[c];
-      }
-      for (int j = 0; j < k; ++j) {
-        uint4* d = xp + (int64_t)f2s[t * k + j] * C;
+      for (int r = 0; r < kCopyRows; ++r)
 #pragma unroll
-        for (int u = 0; u < kCopyUnroll; ++u) {
+        for (int u = 0; u < 2; ++u) {
           const int c = c0 + u * kCopyThreads;
-          if (c < C) d[c] = v[u];
+          if (r < nr && c < C) v[r][u] = x[(t0 + r) * C + c];
+        }
+#pragma unroll
+      for (int r = 0; r < kCopyRows; ++r) {
+        if (r >= nr) break;
+        for (int j = 0; j < k; ++j) {
+          u32x4_t* d = xp + (int64_t)f2s[(t0 + r) * k + j] * C;
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int c = c0 + u * kCopyThreads;
+            if (c < C) __builtin_nontemporal_store(v[r][u], d + c);
+          }
         }
       }
     }
@@ -189,9 +227,10 @@ hipError_t launch_dispatch_copy(const void* x, int64_t M, int64_t row_bytes, int
                                 void* x_perm, hipStream_t s) {
   if (M == 0) return hipSuccess;
   const int C = (int)(row_bytes / 16);
-  const int64_t grid = M < 16384 ? M : 16384;
-  dispatch_copy_kernel<<<(unsigned)grid, kCopyThreads, 0, s>>>((const uint4*)x, M, C, k, flat_to_sorted,
-                                                               (uint4*)x_perm);
+  const int64_t pairs = (M + kCopyRows - 1) / kCopyRows;
+  const int64_t grid = pairs < 16384 ? pairs : 16384;
+  dispatch_copy_kernel<<<(unsigned)grid, kCopyThreads, 0, s>>>((const u32x4_t*)x, M, C, k, flat_to_sorted,
+                                                               (u32x4_t*)x_perm);
   return hipGetLastError();
 }
 

@@ -37,30 +37,67 @@ def build(force: bool = True) -> str:
     return _LIB
 
 
+def _configure(lib):
+    P = ctypes.c_void_p
+    I64, I32 = ctypes.c_int64, ctypes.c_int
+    lib.orc_round_to_bf16.argtypes = [ctypes.c_double]
+    lib.orc_round_to_bf16.restype = ctypes.c_double
+    lib.orc_route.argtypes = [I64, I32, I32, P, P, P]
+    lib.orc_counts_offsets.argtypes = [I64, I32, I32, I32, P, P, P, P]
+    lib.orc_permutation.argtypes = [I64, I32, I32, I32, P, P, P, P]
+    lib.orc_dispatch.argtypes = [I64, I32, I32, I32, P, P, P]
+    lib.orc_ffn_rows.argtypes = [I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, I64, P, P, P]
+    lib.orc_combine_tokens.argtypes = [I32, I32, I64, P, P, P]
+    lib.orc_moe_layer.argtypes = [I64, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, I64, P,
+                                  P, P, P, P, P, P, P, P, P]
+    lib.orc_num_threads.argtypes = []
+    for name in ("orc_route", "orc_counts_offsets", "orc_permutation", "orc_dispatch",
+                 "orc_ffn_rows", "orc_combine_tokens", "orc_moe_layer", "orc_num_threads"):
+        getattr(lib, name).restype = ctypes.c_int
+    return lib
+
+
 def _load():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
             build(force=True)
-        lib = ctypes.CDLL(_LIB)
-        P = ctypes.c_void_p
-        I64, I32 = ctypes.c_int64, ctypes.c_int
-        lib.orc_round_to_bf16.argtypes = [ctypes.c_double]
-        lib.orc_round_to_bf16.restype = ctypes.c_double
-        lib.orc_route.argtypes = [I64, I32, I32, P, P, P]
-        lib.orc_counts_offsets.argtypes = [I64, I32, I32, I32, P, P, P, P]
-        lib.orc_permutation.argtypes = [I64, I32, I32, I32, P, P, P, P]
-        lib.orc_dispatch.argtypes = [I64, I32, I32, I32, P, P, P]
-        lib.orc_ffn_rows.argtypes = [I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, I64, P, P, P]
-        lib.orc_combine_tokens.argtypes = [I32, I32, I64, P, P, P]
-        lib.orc_moe_layer.argtypes = [I64, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, I64, P,
-                                      P, P, P, P, P, P, P, P, P]
-        lib.orc_num_threads.argtypes = []
-        for name in ("orc_route", "orc_counts_offsets", "orc_permutation", "orc_dispatch",
-                     "orc_ffn_rows", "orc_combine_tokens", "orc_moe_layer", "orc_num_threads"):
-            getattr(lib, name).restype = ctypes.c_int
-        _lib = lib
+        _lib = _configure(ctypes.CDLL(_LIB))
     return _lib
+
+
+def build_variant(source_text: str, path: str) -> str:
+    """Compile another copy of the oracle source (the mutation tests plant
+    mistakes in such copies to show the pins catch them)."""
+    src = path + ".c"
+    with open(src, "w") as fh:
+        fh.write(source_text)
+    subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-shared",
+                    "-fPIC", src, "-o", path, "-lm"], check=True)
+    return path
+
+
+class use_library:
+    """Context manager: route every call of this module to another build."""
+
+    def __init__(self, path: str):
+        self.lib = _configure(ctypes.CDLL(path))
+
+    def __enter__(self):
+        global _lib
+        self.saved = _load()
+        _lib = self.lib
+        return self
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
+        return False
+
+
+def source_text() -> str:
+    with open(_SRC) as fh:
+        return fh.read()
 
 
 def _p(a):

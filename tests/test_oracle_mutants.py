@@ -1,0 +1,95 @@
+"""The oracle's pins catch plausible mistakes (CPU only).
+
+Each case plants one mistake in a copy of the oracle's C source -- a flipped
+tie rule, a dropped normalisation, swapped gate/up, a transposed weight, a
+wrong index into the permutation, an unstable order, a wrong segment key --
+builds it, routes the oracle module to that build, and runs the pin checks
+of tests/test_oracle_pins.py.  At least one pin must fail for every mutant;
+the unmodified source must pass them all.
+"""
+import os
+
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+MUTANTS = {
+    "ties_to_higher_index": ("if (best < 0 || row[e] > row[best]) best = e;",
+                             "if (best < 0 || row[e] >= row[best]) best = e;"),
+    "weights_not_normalised": ("exp((double)row[sel[j]] - l0) / denom)", "exp((double)row[sel[j]] - l0))"),
+    "weights_unshifted_slot": ("topk_w[t * k + j] = (float)(exp((double)row[sel[j]] - l0) / denom);",
+                               "topk_w[t * k + j] = (float)(exp((double)row[sel[0]] - l0) / denom);"),
+    "gate_up_swapped": ("double a = silu(g) * u;", "double a = silu(u) * g;"),
+    "silu_sign": ("static double silu(double z) { return z / (1.0 + exp(-z)); }",
+                  "static double silu(double z) { return z / (1.0 + exp(z)); }"),
+    "no_bf16_rounding": ("hact[f] = (dtype == ORC_BF16) ? orc_round_to_bf16(a) : a;", "hact[f] = a;"),
+    "bf16_rounds_to_zero": ("double r = nearbyint(scaled);", "double r = trunc(scaled);"),
+    "down_transposed": ("for (int f = 0; f < F; ++f) acc += hact[f] * load_elem(w_down, dtype, wrow + f);",
+                        "for (int f = 0; f < F; ++f) acc += hact[f] * load_elem(w_down, dtype, eHF + (int64_t)f * H + n);"),
+    "gate_transposed": ("g += xrow[h] * load_elem(w_gate, dtype, wrow + h);",
+                        "g += xrow[h] * load_elem(w_gate, dtype, eHF + (int64_t)h * F + f);"),
+    "combine_slot0_weight": ("acc += (double)topk_w_sub[i * k + j] * y_rows[(i * k + j) * H + n];",
+                             "acc += (double)topk_w_sub[i * k] * y_rows[(i * k + j) * H + n];"),
+    "combine_drops_last_slot": ("for (int j = 0; j < k; ++j) acc += (double)topk_w_sub",
+                                "for (int j = 0; j + 1 < k; ++j) acc += (double)topk_w_sub"),
+    "unstable_permutation": ("for (int64_t f = 0; f < R; ++f)\n      if (seg_of(topk_idx, src_block, E, k, f) == g) sorted_to_flat[r++] = (int32_t)f;",
+                             "for (int64_t f = R - 1; f >= 0; --f)\n      if (seg_of(topk_idx, src_block, E, k, f) == g) sorted_to_flat[r++] = (int32_t)f;"),
+    "segment_key_unscaled": ("return s * E + topk_idx[f];", "return s + topk_idx[f];"),
+    "expert_from_block_index": ("int e = (int)(g % E);", "int e = (int)((g / E) % E);"),
+    "ffn_reads_flat_row": ("int64_t t = sorted_to_flat[r] / k;\n    double* xrow", "int64_t t = r / k;\n    double* xrow"),
+    "dispatch_wrong_token": ("int64_t t = sorted_to_flat[r] / k;\n    memcpy", "int64_t t = sorted_to_flat[r] % k;\n    memcpy"),
+    "inverse_not_inverted": ("flat_to_sorted[sorted_to_flat[q]] = (int32_t)q;", "flat_to_sorted[q] = sorted_to_flat[q];"),
+    "offsets_inclusive": ("offsets[g + 1] = offsets[g] + counts[g];", "offsets[g + 1] = offsets[g] + counts[g] + (g == 0);"),
+}
+
+
+def _checks():
+    """The pin checks, as callables that raise on failure."""
+    return [
+        ("bf16", pins.test_bf16_rounding_matches_torch),
+        ("route_E8", lambda: pins.test_route_matches_python_sort(8, 2)),
+        ("route_E64", lambda: pins.test_route_matches_python_sort(64, 4)),
+        ("k2_closed_form", pins.test_route_weights_closed_form_k2),
+        ("softmax", pins.test_route_weights_full_softmax_renormalised),
+        ("k1", pins.test_route_k1_weight_is_exactly_one),
+        ("segments_S1", lambda: pins.test_segments_and_permutation_brute_force(37, 8, 2, 1)),
+        ("segments_S8", lambda: pins.test_segments_and_permutation_brute_force(96, 16, 8, 8)),
+        ("dispatch", pins.test_dispatch_is_bitwise_row_copy),
+        ("dense_f32", lambda: pins.test_layer_matches_dense_brute_force("f32", 4, 2)),
+        ("dense_bf16", lambda: pins.test_layer_matches_dense_brute_force("bf16", 6, 3)),
+        ("dense_src_blocks", pins.test_layer_with_source_blocks_matches_dense),
+        ("single_ffn", pins.test_top1_single_expert_is_one_dense_swiglu_ffn),
+    ]
+
+
+def _failures():
+    failed = []
+    for name, fn in _checks():
+        try:
+            fn()
+        except (AssertionError, ValueError, IndexError):
+            failed.append(name)
+    return failed
+
+
+@pytest.fixture(scope="module")
+def workdir(tmp_path_factory):
+    return tmp_path_factory.mktemp("oracle_mutants")
+
+
+def test_unmodified_source_passes_every_check(workdir):
+    path = oracle.build_variant(oracle.source_text(), os.path.join(workdir, "orc_clean.so"))
+    with oracle.use_library(path):
+        assert _failures() == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(workdir, name):
+    old, new = MUTANTS[name]
+    src = oracle.source_text()
+    assert src.count(old) == 1, f"mutation anchor not unique for {name}"
+    path = oracle.build_variant(src.replace(old, new), os.path.join(workdir, f"orc_{name}.so"))
+    with oracle.use_library(path):
+        failed = _failures()
+    assert failed, f"no pin caught the planted mistake {name}"

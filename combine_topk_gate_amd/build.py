@@ -33,7 +33,7 @@ def hipcc() -> str:
 
 
 def compile_flags() -> list:
-    return ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-Wall", "-Wno-unused-command-line-argument",
+    return ["-O3", "-std=c++20", f"--offload-arch={ARCH}", "-fPIC", "-Wall", "-Wno-unused-command-line-argument",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 

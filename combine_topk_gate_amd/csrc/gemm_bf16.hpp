@@ -130,8 +130,12 @@ __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int
   // Global loads in 4 parts (one per k16 sub-step of the MFMA loop); part q
   // covers the thread's weight rows lr + 32 i, i in {2q, 2q+1}, and token
   // rows lr + 32 i, i in [q XQ, (q+1) XQ).
+  // With `pin`, each load is fenced from the scheduler so the loads issue in
+  // source order: the prologue must issue stage 1 in the loop body's order,
+  // or the wait-count pass, which merges the prologue and the loop's back
+  // edge at the loop header, makes every iteration wait for the later loads.
   i32x4_t wreg[8], xreg[XI];
-  auto gload_part = [&](int kt, int q) {
+  auto gload_part = [&](int kt, int q, bool pin = false) {
     const uint32_t soff = (uint32_t)kt * (kBK * 2);
 #pragma unroll
     for (int i = 2 * q; i < 2 * q + 2; ++i) {
@@ -139,9 +143,13 @@ __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int
         wreg[i] = buf_load16(i < 4 ? rw0 : rw1, voff0 + (uint32_t)(i & 3) * vstep, soff);
       else
         wreg[i] = buf_load16(rw0, voff0 + (uint32_t)i * vstep, soff);
+      if (pin) __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int i = q * XQ; i < (q + 1) * XQ; ++i) xreg[i] = buf_load16(rx, xvoff[i], soff);
+    for (int i = q * XQ; i < (q + 1) * XQ; ++i) {
+      xreg[i] = buf_load16(rx, xvoff[i], soff);
+      if (pin) __builtin_amdgcn_sched_barrier(0);
+    }
   };
   auto lstore_part = [&](int stage, int q) {
     char* wdst = lds + stage * kStageBytes + st_off;
@@ -203,7 +211,7 @@ __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int
   for (int q = 0; q < 4; ++q) lstore_part(0, q);
   const int k1 = nk > 1 ? 1 : 0;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) gload_part(k1, q);
+  for (int q = 0; q < 4; ++q) gload_part(k1, q, true);
   __syncthreads();
   read_frags(0, 0, 0);
 
@@ -288,49 +296,87 @@ __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // ---- epilogue: lane holds column block 8q + 4 lk + (0..3) of token row lrow
+  // ---- epilogue.  Lane (lrow, lk) holds, per token fragment nj and weight
+  // fragment mi, the 4-column groups 8q + 4 lk (q = 0..3) of token row
+  // wm*TM/2 + 32 nj + lrow.  Stored straight from there, every store would
+  // touch 32 rows; the tile is staged through LDS instead, so each wave
+  // stores whole 256 B (Hact) or 1 KiB (Y) row segments.  After the loop's
+  // last barrier no wave reads a value from either LDS buffer again (the
+  // next-stage reads of the last iteration are discarded), so both are free.
   if (LAYER == 0) {
-    __bf16* hact = reinterpret_cast<__bf16*>(p.c);
+    // 256 B per staged row (128 bf16 columns); 8-byte unit u of row t at
+    // unit u ^ (t & 31): conflict-free for 32 rows writing the same unit.
+    char* stg = lds;
 #pragma unroll
     for (int nj = 0; nj < NJ; ++nj) {
-      const int trow = m0 + wm * (TM / 2) + nj * 32 + lrow;
-      if (trow >= seg_rows) continue;
-      __bf16* dst = hact + (int64_t)(seg_start + trow) * N;
+      const int t = wm * (TM / 2) + nj * 32 + lrow;
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int f = col0 + wn * 64 + mi * 32 + 8 * q + 4 * lk;
-          if (f >= N) continue;
           bf16x4_t h;
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
             const float gt = acc[mi][nj][4 * q + v], up = acc[mi + 2][nj][4 * q + v];
             h[v] = (__bf16)silu_mul_fast(gt, up);
           }
-          *reinterpret_cast<bf16x4_t*>(dst + f) = h;
+          const int u = wn * 16 + mi * 8 + 2 * q + lk;
+          *reinterpret_cast<bf16x4_t*>(stg + t * 256 + ((u ^ (t & 31)) << 3)) = h;
         }
       }
     }
+    __syncthreads();
+    // 16 threads per row, 16 B (8 columns) each: chunk c of row t sits at
+    // chunk c ^ ((t & 31) >> 1), its two halves swapped when t is odd.
+    __bf16* hact = reinterpret_cast<__bf16*>(p.c);
+    const int c = tid & 15;
+    const int f = col0 + 8 * c;
+#pragma unroll 4
+    for (int t = tid >> 4; t < TM; t += kGemmThreads / 16) {
+      i32x4_t v = *reinterpret_cast<const i32x4_t*>(stg + t * 256 + ((c ^ ((t & 31) >> 1)) << 4));
+      if (t & 1) v = i32x4_t{v[2], v[3], v[0], v[1]};
+      const int trow = m0 + t;
+      if (trow < seg_rows && f < N)
+        *reinterpret_cast<i32x4_t*>(hact + (int64_t)(seg_start + trow) * N + f) = v;
+    }
+    __syncthreads();
   } else {
+    // Two passes of 128 rows (one for a half tile), 1 KiB per staged row (256
+    // f32 columns) over both buffers; 16-byte unit u of staged row t' at unit
+    // u ^ (t' & 15).  Pass P stages token fragments nj = 2P, 2P + 1: staged
+    // row t' = wm*64 + (nj & 1)*32 + lrow is tile row wm*TM/2 + 64 P + t' % 64.
     float* y = reinterpret_cast<float*>(p.c);
+    char* stg = lds;
+    constexpr int passes = NJ / 2;
 #pragma unroll
-    for (int nj = 0; nj < NJ; ++nj) {
-      const int trow = m0 + wm * (TM / 2) + nj * 32 + lrow;
-      if (trow >= seg_rows) continue;
-      float* dst = y + (int64_t)(seg_start + trow) * N;
+    for (int P = 0; P < passes; ++P) {
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
+      for (int j = 0; j < 2; ++j) {
+        const int nj = 2 * P + j;
+        const int ts = wm * 64 + j * 32 + lrow;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = col0 + wn * 128 + mi * 32 + 8 * q + 4 * lk;
-          if (n >= N) continue;
-          f32x4_t o;
+        for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
-          for (int v = 0; v < 4; ++v) o[v] = acc[mi][nj][4 * q + v];
-          *reinterpret_cast<f32x4_t*>(dst + n) = o;
+          for (int q = 0; q < 4; ++q) {
+            f32x4_t o;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) o[v] = acc[mi][nj][4 * q + v];
+            const int u = wn * 32 + mi * 8 + 2 * q + lk;
+            *reinterpret_cast<f32x4_t*>(stg + ts * 1024 + ((u ^ (ts & 15)) << 4)) = o;
+          }
         }
       }
+      __syncthreads();
+      // 64 threads per staged row, 16 B (4 columns) each
+      const int c = tid & 63;
+      const int n = col0 + 4 * c;
+#pragma unroll 4
+      for (int ts = tid >> 6; ts < 128; ts += kGemmThreads / 64) {
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stg + ts * 1024 + ((c ^ (ts & 15)) << 4));
+        const int trow = m0 + (ts >> 6) * (TM / 2) + 64 * P + (ts & 63);
+        if (trow < seg_rows && n < N) *reinterpret_cast<f32x4_t*>(y + (int64_t)(seg_start + trow) * N + n) = v;
+      }
+      __syncthreads();
     }
   }
 }

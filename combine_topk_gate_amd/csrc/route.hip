@@ -5,28 +5,35 @@
 // accumulation): each token keeps its k largest gate logits, and the
 // weights are the softmax over the k chosen logits.
 //
-// One wave handles 64 tokens, one token per lane.  The wave stages its
-// 64 x E logits through LDS in chunks of 64 experts so the HBM reads are
-// coalesced, then every lane walks its row in increasing expert order and
-// keeps the KMAX best (value, index) pairs sorted in registers.  A new value
-// enters only if it is strictly greater than the current KMAX-th value and
-// goes behind every kept value it does not exceed, so equal logits keep the
-// lower index first.
+// Sixteen lanes handle one token (a 256-thread block: 16 tokens).  Lane q
+// reads experts q, q + 16, q + 32, ... (the 16 lanes of a token read 64
+// consecutive bytes at a time) and keeps its KMAX best (value, index) pairs
+// sorted in registers.  The lanes' lists are then merged in four butterfly
+// steps: partners exchange their lists and both keep the KMAX best of the
+// union.  "Best" is the total order value descending, then index ascending,
+// which is the order the selection defines (equal logits keep the lower
+// expert index first), so the merged list is unique and every lane of the
+// token ends with the same one.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace moe {
 
-constexpr int kRouteTokens = 64;
-constexpr int kRouteChunk = 64;
+constexpr int kRouteThreads = 256;
+constexpr int kLanesPerToken = 16;
+
+// a ahead of b: larger value, or equal value and lower index
+__device__ __forceinline__ bool route_before(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
 
 template <int KMAX>
 __device__ __forceinline__ void topk_insert(float (&vals)[KMAX], int (&ids)[KMAX], float v, int e) {
+  // e exceeds every index kept so far, so v enters only if strictly larger
+  // than the last kept value, behind every kept value it does not exceed
   if (!(v > vals[KMAX - 1])) return;
 #pragma unroll
   for (int i = KMAX - 1; i >= 0; --i) {
-    // position i keeps its value if that value is >= v; otherwise it takes
-    // v (if the slot above it is >= v, or i == 0) or the value from above.
     if (vals[i] >= v) continue;
     const bool above_ge = (i == 0) ? true : (vals[i - 1] >= v);
     if (above_ge) {
@@ -39,39 +46,78 @@ __device__ __forceinline__ void topk_insert(float (&vals)[KMAX], int (&ids)[KMAX
   }
 }
 
+// Keep the KMAX best of two sorted lists (own and the partner lane's):
+// pairing own[i] with partner[KMAX-1-i] and keeping the better of each pair
+// leaves the KMAX best as a bitonic sequence, which a bitonic merger sorts.
 template <int KMAX>
-__global__ __launch_bounds__(kRouteTokens) void route_topk_kernel(const float* __restrict__ logits, int64_t M, int E,
+__device__ __forceinline__ void topk_merge_partner(float (&vals)[KMAX], int (&ids)[KMAX], int off) {
+  float pv[KMAX];
+  int pi[KMAX];
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) {
+    pv[i] = __shfl_xor(vals[i], off);
+    pi[i] = __shfl_xor(ids[i], off);
+  }
+#pragma unroll
+  for (int i = 0; i < KMAX; ++i) {
+    const float bv = pv[KMAX - 1 - i];
+    const int bi = pi[KMAX - 1 - i];
+    if (!route_before(vals[i], ids[i], bv, bi)) {
+      vals[i] = bv;
+      ids[i] = bi;
+    }
+  }
+#pragma unroll
+  for (int half = KMAX / 2; half >= 1; half >>= 1) {
+#pragma unroll
+    for (int i = 0; i < KMAX; ++i) {
+      if (i & half) continue;
+      const int j = i + half;
+      if (!route_before(vals[i], ids[i], vals[j], ids[j])) {
+        const float tv = vals[i];
+        const int ti = ids[i];
+        vals[i] = vals[j];
+        ids[i] = ids[j];
+        vals[j] = tv;
+        ids[j] = ti;
+      }
+    }
+  }
+}
+
+template <int KMAX>
+__global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float* __restrict__ logits, int64_t M, int E,
                                                                    int k, int32_t* __restrict__ topk_idx,
                                                                    float* __restrict__ topk_w) {
-  __shared__ float tile[kRouteTokens][kRouteChunk + 1];
-  const int lane = threadIdx.x;
-  const int64_t t0 = (int64_t)blockIdx.x * kRouteTokens;
-  const int ntok = (int)((M - t0) < kRouteTokens ? (M - t0) : kRouteTokens);
-
+  const int q = threadIdx.x % kLanesPerToken;
+  const int64_t t = (int64_t)blockIdx.x * (kRouteThreads / kLanesPerToken) + threadIdx.x / kLanesPerToken;
+  const bool valid = t < M;  // whole 16-lane groups share `valid`
   float vals[KMAX];
   int ids[KMAX];
 #pragma unroll
   for (int i = 0; i < KMAX; ++i) {
     vals[i] = -__builtin_inff();
-    ids[i] = 0;
+    ids[i] = 0x7fffffff;  // behind every real expert (logits are finite)
   }
-
-  for (int c0 = 0; c0 < E; c0 += kRouteChunk) {
-    const int ce = (E - c0) < kRouteChunk ? (E - c0) : kRouteChunk;
-    const int n = ntok * ce;
-    for (int i = lane; i < n; i += kRouteTokens) {
-      const int tt = i / ce, ee = i - tt * ce;
-      tile[tt][ee] = logits[(t0 + tt) * (int64_t)E + c0 + ee];
+  if (valid) {
+    const float* row = logits + t * (int64_t)E;
+    // 4 loads in flight per lane, then insertion in increasing expert order
+    int e = q;
+    for (; e + 3 * kLanesPerToken < E; e += 4 * kLanesPerToken) {
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = row[e + u * kLanesPerToken];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) topk_insert<KMAX>(vals, ids, v[u], e + u * kLanesPerToken);
     }
-    __syncthreads();
-    if (lane < ntok) {
-      for (int ee = 0; ee < ce; ++ee) topk_insert<KMAX>(vals, ids, tile[lane][ee], c0 + ee);
-    }
-    __syncthreads();
+    for (; e < E; e += kLanesPerToken) topk_insert<KMAX>(vals, ids, row[e], e);
   }
-  if (lane >= ntok) return;
+#pragma unroll
+  for (int off = 1; off < kLanesPerToken; off <<= 1) topk_merge_partner<KMAX>(vals, ids, off);
+  if (!valid) return;
 
-  const int64_t t = t0 + lane;
+  // weights: softmax over the k chosen logits, shifted by the largest,
+  // summed in slot order; lane j < k writes slot j
   const float l0 = vals[0];
   float denom = 0.0f;
 #pragma unroll
@@ -79,7 +125,7 @@ __global__ __launch_bounds__(kRouteTokens) void route_topk_kernel(const float* _
     if (j < k) denom += expf(vals[j] - l0);
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
-    if (j < k) {
+    if (j < k && j == q) {
       topk_idx[t * k + j] = ids[j];
       topk_w[t * k + j] = expf(vals[j] - l0) / denom;
     }
@@ -89,7 +135,8 @@ __global__ __launch_bounds__(kRouteTokens) void route_topk_kernel(const float* _
 hipError_t launch_route(const float* logits, int64_t M, int E, int k, int32_t* topk_idx, float* topk_w,
                         hipStream_t s) {
   if (M == 0) return hipSuccess;
-  const dim3 grid((unsigned)((M + kRouteTokens - 1) / kRouteTokens)), block(kRouteTokens);
+  const int64_t per_block = kRouteThreads / kLanesPerToken;
+  const dim3 grid((unsigned)((M + per_block - 1) / per_block)), block(kRouteThreads);
   if (k <= 1)
     route_topk_kernel<1><<<grid, block, 0, s>>>(logits, M, E, k, topk_idx, topk_w);
   else if (k <= 2)

@@ -35,6 +35,7 @@
 
 #include "common.hpp"
 
+
 namespace moe {
 
 constexpr int kGemmThreads = 256;
@@ -159,6 +160,28 @@ __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int
 #pragma unroll
     for (int i = q * XQ; i < (q + 1) * XQ; ++i) *reinterpret_cast<i32x4_t*>(xdst + i * 4096) = xreg[i];
   };
+  // single operations of part q (TM = 256: 2 weight and 2 token rows each),
+  // for schedules that interleave stores, loads and fragment reads one by one
+  auto lstore_one = [&](int stage, int q, int j) {
+    char* wdst = lds + stage * kStageBytes + st_off;
+    if (j < 2)
+      *reinterpret_cast<i32x4_t*>(wdst + (2 * q + j) * 4096) = wreg[2 * q + j];
+    else
+      *reinterpret_cast<i32x4_t*>(wdst + kOperandBytes + (q * XQ + j - 2) * 4096) = xreg[q * XQ + j - 2];
+  };
+  auto gload_one = [&](int kt, int q, int j) {
+    const uint32_t soff = (uint32_t)kt * (kBK * 2);
+    if (j < 2) {
+      const int i = 2 * q + j;
+      if (LAYER == 0)
+        wreg[i] = buf_load16(i < 4 ? rw0 : rw1, voff0 + (uint32_t)(i & 3) * vstep, soff);
+      else
+        wreg[i] = buf_load16(rw0, voff0 + (uint32_t)i * vstep, soff);
+    } else {
+      const int i = q * XQ + j - 2;
+      xreg[i] = buf_load16(rx, xvoff[i], soff);
+    }
+  };
 
   // ---- fragment addressing
   const int lrow = lane & 31, lk = lane >> 5;
@@ -177,14 +200,27 @@ __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int
   // two register sets of fragments: sub-step ks uses set ks & 1 while the
   // reads for ks + 1 fill the other set
   bf16x8_t fa[2][4], fb[2][NJ];
+  // fragment j of sub-step ks in the order the MFMAs use them: weight 0,
+  // the token fragments, weights 1..3
+  auto read_one = [&](int set, int stage, int ks, int j) {
+    const char* base = lds + stage * kStageBytes;
+    if (j == 0)
+      fa[set][0] = *reinterpret_cast<const bf16x8_t*>(base + wrow_off[0] + kswz[ks]);
+    else if (j <= NJ)
+      fb[set][j - 1] = *reinterpret_cast<const bf16x8_t*>(base + xrow_off + (j - 1) * 4096 + kswz[ks]);
+    else
+      fa[set][j - NJ] = *reinterpret_cast<const bf16x8_t*>(base + wrow_off[j - NJ] + kswz[ks]);
+  };
   auto read_frags = [&](int set, int stage, int ks) {
     const char* base = lds + stage * kStageBytes;
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-      fa[set][mi] = *reinterpret_cast<const bf16x8_t*>(base + wrow_off[mi] + kswz[ks]);
+    // in the order the next sub-step's MFMAs (weight fragment outer) use them
+    fa[set][0] = *reinterpret_cast<const bf16x8_t*>(base + wrow_off[0] + kswz[ks]);
 #pragma unroll
     for (int nj = 0; nj < NJ; ++nj)
       fb[set][nj] = *reinterpret_cast<const bf16x8_t*>(base + xrow_off + nj * 4096 + kswz[ks]);
+#pragma unroll
+    for (int mi = 1; mi < 4; ++mi)
+      fa[set][mi] = *reinterpret_cast<const bf16x8_t*>(base + wrow_off[mi] + kswz[ks]);
   };
 
   f32x16_t acc[4][NJ];
@@ -238,23 +274,34 @@ __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int
     const int kload = (kt + 2 < nk) ? kt + 2 : nk - 1;
 #pragma unroll
     for (int ks = 0; ks < 3; ++ks) {
-      read_frags((ks + 1) & 1, cur, ks + 1);
-      lstore_part(nxt, ks);
-      gload_part(kload, ks);
+      if constexpr (TM == 256) {
+        // source order = issue order: LDS operations keep their order (the
+        // compiler cannot tell the two buffers apart)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          read_one((ks + 1) & 1, cur, ks + 1, 2 * j);
+          lstore_one(nxt, ks, j);
+          read_one((ks + 1) & 1, cur, ks + 1, 2 * j + 1);
+          gload_one(kload, ks, j);
+        }
+      } else {
+        read_frags((ks + 1) & 1, cur, ks + 1);
+        lstore_part(nxt, ks);
+        gload_part(kload, ks);
+      }
       mfma_rows(ks & 1, 0, 4);
       if constexpr (TM == 256) {
+        // one memory operation after every MFMA: fragment reads in the even
+        // slots, LDS stores in slots 1, 5, 9, 13, loads in 3, 7, 11, 15 (a
+        // burst of LDS stores stalls the matrix core of the issuing wave)
 #pragma unroll
-        for (int i = 0; i < NR; ++i) {
+        for (int i = 0; i < 4; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-        }
-#pragma unroll
-        for (int i = 0; i < NW; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
           __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
-        }
-#pragma unroll
-        for (int i = 0; i < NW; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
           __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
         }
@@ -276,12 +323,26 @@ __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int
     lstore_part(nxt, 3);
     gload_part(kload, 3);
     mfma_rows(1, 0, 2);
+    if constexpr (TM == 256) {
+      // the stores first (they must land before the barrier), then the loads
 #pragma unroll
-    for (int i = 0; i < NM / 2; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x220, 1, 0);  // DS write or VMEM read
+      for (int i = 0; i < NW; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+      }
+#pragma unroll
+      for (int i = 0; i < NW; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NM / 2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x220, 1, 0);  // DS write or VMEM read
+      }
+      if constexpr (2 * NW > NM / 2) __builtin_amdgcn_sched_group_barrier(0x220, 2 * NW - NM / 2, 0);
     }
-    if constexpr (2 * NW > NM / 2) __builtin_amdgcn_sched_group_barrier(0x220, 2 * NW - NM / 2, 0);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);

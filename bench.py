@@ -101,12 +101,21 @@ def cpu_baseline(cfg, d, target_s):
     import moe_synth
     import oracle
     flop_tok = 6.0 * cfg.k * cfg.H * cfg.F
-    probe = moe_synth.token_sample(cfg, max(cfg.S, 2), seed_tag=11)
-    t0 = time.perf_counter()
-    oracle.moe_layer(d["x"], d["logits"], d["w_gate"], d["w_up"], d["w_down"], cfg.k, S=cfg.S,
-                     src_block=d["src_block"], tokens=probe)
-    dt_probe = time.perf_counter() - t0
-    n = int(max(cfg.S, min(cfg.M, round(len(probe) * target_s / max(dt_probe, 1e-3)))))
+
+    def timed(n_tok, tag):
+        toks = moe_synth.token_sample(cfg, n_tok, seed_tag=tag)
+        t0 = time.perf_counter()
+        oracle.moe_layer(d["x"], d["logits"], d["w_gate"], d["w_up"], d["w_down"], cfg.k, S=cfg.S,
+                         src_block=d["src_block"], tokens=toks)
+        return len(toks), time.perf_counter() - t0
+
+    # two probe sizes separate the fixed cost (full routing of every token)
+    # from the per-token FFN cost, so the sample lands near target_s
+    n1, t1 = timed(max(cfg.S, 2), 11)
+    n2, t2 = timed(max(cfg.S, 16), 13)
+    per_tok = max((t2 - t1) / max(n2 - n1, 1), 1e-6)
+    fixed = max(t1 - n1 * per_tok, 0.0)
+    n = int(max(cfg.S, min(cfg.M, round((target_s - fixed) / per_tok))))
     toks = moe_synth.token_sample(cfg, n, seed_tag=12)
     t0 = time.perf_counter()
     oracle.moe_layer(d["x"], d["logits"], d["w_gate"], d["w_up"], d["w_down"], cfg.k, S=cfg.S,

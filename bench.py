@@ -172,6 +172,8 @@ def main():
     out = torch.empty((M, H), dtype=torch.float32, device=dev)
     ws_d = torch.empty(max(4, moe.moe_workspace_bytes(p, moe.MOE_OP_DISPATCH)), dtype=torch.uint8, device=dev)
     ws_l = torch.empty(moe.moe_workspace_bytes(p, moe.MOE_OP_LAYER), dtype=torch.uint8, device=dev)
+    n_gws = moe.moe_workspace_bytes(p, moe.MOE_OP_GROUPED_GEMM)
+    ws_g = torch.empty(n_gws, dtype=torch.uint8, device=dev) if n_gws > 0 else None
     stream = torch.cuda.current_stream()
     src = g.get("src_block")
 
@@ -197,9 +199,9 @@ def main():
         if ev: ev[1].record(stream)
         moe.moe_dispatch(p, g["x"], idx, src, counts, offsets, s2f, f2s, xp, ws_d, stream)
         if ev: ev[2].record(stream)
-        moe.moe_grouped_gemm(p, 0, xp, g["w_gate"], g["w_up"], offsets, hact, None, stream)
+        moe.moe_grouped_gemm(p, 0, xp, g["w_gate"], g["w_up"], offsets, hact, ws_g, stream)
         if ev: ev[3].record(stream)
-        moe.moe_grouped_gemm(p, 1, hact, g["w_down"], None, offsets, y, None, stream)
+        moe.moe_grouped_gemm(p, 1, hact, g["w_down"], None, offsets, y, ws_g, stream)
         if ev: ev[4].record(stream)
         moe.moe_combine(p, y, w, f2s, out, stream)
         if ev: ev[5].record(stream)

@@ -41,7 +41,7 @@ moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ER
 
 // Workspace of the whole layer, carved in this order (each region 256-B aligned).
 struct LayerWs {
-  size_t status, topk_idx, topk_w, counts, offsets, s2f, f2s, perm, x_perm, hact, y, fused, total;
+  size_t status, topk_idx, topk_w, counts, offsets, s2f, f2s, perm, x_perm, hact, y, fused, gemm, total;
 };
 
 LayerWs layer_ws(const moe_problem_t* p) {
@@ -64,6 +64,7 @@ LayerWs layer_ws(const moe_problem_t* p) {
   w.y = o; o += align_up((size_t)R * p->hidden * 4);
   w.fused = o; o += align_up(fused_ws_bytes(p->num_tokens, p->hidden, p->ffn, p->num_experts, p->topk,
                                              p->num_src_blocks));
+  w.gemm = o; o += align_up(p->dtype == MOE_DTYPE_BF16 ? gemm_split_ws_bytes() : 0);
   w.total = o;
   return w;
 }
@@ -96,7 +97,7 @@ size_t moe_workspace_bytes(const moe_problem_t* p, int32_t op) {
   const int G = p->num_src_blocks * p->num_experts;
   switch (op) {
     case MOE_OP_DISPATCH: return permute_ws_bytes(permute_plan(p->num_tokens, p->topk, G));
-    case MOE_OP_GROUPED_GEMM: return 0;
+    case MOE_OP_GROUPED_GEMM: return p->dtype == MOE_DTYPE_BF16 ? gemm_split_ws_bytes() : 0;
     case MOE_OP_LAYER: return layer_ws(p).total;
   }
   return 0;
@@ -137,8 +138,6 @@ moe_status_t moe_dispatch(const moe_problem_t* p, const void* x, const int32_t* 
 
 moe_status_t moe_grouped_gemm(const moe_problem_t* p, int32_t layer, const void* a, const void* w0, const void* w1,
                               const int32_t* offsets, void* c, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   moe_status_t st = check_problem(p);
   if (st != MOE_OK) return st;
   if (layer != 0 && layer != 1) return MOE_ERR_INVALID_ARGUMENT;
@@ -159,6 +158,11 @@ moe_status_t moe_grouped_gemm(const moe_problem_t* p, int32_t layer, const void*
   gp.N = layer == 0 ? p->ffn : p->hidden;
   gp.E = p->num_experts;
   gp.G = p->num_src_blocks * p->num_experts;
+  // a workspace smaller than moe_workspace_bytes(p, MOE_OP_GROUPED_GEMM)
+  // (or none) only disables the split of the last round
+  if (ws && !aligned(ws, 16)) return MOE_ERR_INVALID_ARGUMENT;
+  gp.ws = ws;
+  gp.ws_bytes = ws ? ws_bytes : 0;
   hipStream_t s = (hipStream_t)stream;
   return hip_status(p->dtype == MOE_DTYPE_BF16 ? launch_grouped_gemm_bf16(gp, s) : launch_grouped_gemm_f32(gp, s));
 }
@@ -293,6 +297,8 @@ moe_status_t moe_layer(const moe_problem_t* p, const void* x, const float* logit
   gp.c = hact;
   gp.K = p->hidden;
   gp.N = p->ffn;
+  gp.ws = at<void>(ws, L.gemm);
+  gp.ws_bytes = L.total - L.gemm;
   e = p->dtype == MOE_DTYPE_BF16 ? launch_grouped_gemm_bf16(gp, s) : launch_grouped_gemm_f32(gp, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   gp.layer = 1;

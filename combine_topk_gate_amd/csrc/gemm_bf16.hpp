@@ -72,10 +72,16 @@ __device__ __forceinline__ i32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-template <int LAYER, bool GATHER = false, int TM = kTileRows>
+// PARTIAL (layer 1): compute only K steps [k0, k1) and store the raw f32
+// accumulators of the tile to part[t * 256 + w] (t = tile token row < trows,
+// w = the tile's weight row); the caller adds the K ranges of a tile in a
+// fixed order.  Otherwise k0 = 0, k1 = K / kBK (the whole reduction).
+template <int LAYER, bool GATHER = false, int TM = kTileRows, bool PARTIAL = false>
 __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int seg_start, int seg_rows, int m0,
-                                               int nt, char* __restrict__ lds) {
+                                               int nt, char* __restrict__ lds, int k0 = 0, int k1 = -1,
+                                               float* __restrict__ part = nullptr) {
   static_assert(TM == 256 || TM == 128, "token tile height");
+  static_assert(!PARTIAL || (TM == 256 && LAYER == 1), "partial tiles: layer 1, full height");
   constexpr int NJ = TM / 64;      // token fragments per wave
   constexpr int XI = TM / 32;      // token-row loads per thread per K step
   constexpr int XQ = XI / 4;       // ... per sub-step
@@ -239,15 +245,17 @@ __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int
         acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[set][mi], fb[set][nj], acc[mi][nj], 0, 0, 0);
   };
 
-  const int nk = K / kBK;
-  // prologue: stage 0 into LDS, stage 1 into registers, fragments of (0, 0)
+  // K steps [kb, nk) of 64
+  const int nk = uniform(k1 < 0 ? K / kBK : k1);
+  const int kb = uniform(k0);
+  // prologue: stage kb into LDS, stage kb + 1 into registers, fragments of (kb, 0)
 #pragma unroll
-  for (int q = 0; q < 4; ++q) gload_part(0, q);
+  for (int q = 0; q < 4; ++q) gload_part(kb, q);
 #pragma unroll
   for (int q = 0; q < 4; ++q) lstore_part(0, q);
-  const int k1 = nk > 1 ? 1 : 0;
+  const int kb1 = nk > kb + 1 ? kb + 1 : kb;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) gload_part(k1, q, true);
+  for (int q = 0; q < 4; ++q) gload_part(kb1, q, true);
   __syncthreads();
   read_frags(0, 0, 0);
 
@@ -269,8 +277,8 @@ __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int
   constexpr int NR = 4 + NJ;        // fragment reads per sub-step
   constexpr int NW = 2 + XQ;        // LDS stores (and loads) per sub-step
   constexpr int NM = 4 * NJ;        // MFMAs per sub-step
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1, nxt = cur ^ 1;
+  for (int kt = kb; kt < nk; ++kt) {
+    const int cur = (kt - kb) & 1, nxt = cur ^ 1;
     const int kload = (kt + 2 < nk) ? kt + 2 : nk - 1;
 #pragma unroll
     for (int ks = 0; ks < 3; ++ks) {
@@ -364,7 +372,41 @@ __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int
   // stores whole 256 B (Hact) or 1 KiB (Y) row segments.  After the loop's
   // last barrier no wave reads a value from either LDS buffer again (the
   // next-stage reads of the last iteration are discarded), so both are free.
-  if (LAYER == 0) {
+  if (PARTIAL) {
+    // raw accumulators, staged as in the layer-1 epilogue: two passes of 128
+    // rows, 1 KiB per staged row (256 f32 values, one per weight row of the
+    // tile); 16-byte unit u of staged row t' at unit u ^ (t' & 15)
+    char* stg = lds;
+#pragma unroll
+    for (int P = 0; P < 2; ++P) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int nj = 2 * P + j;
+        const int ts = wm * 64 + j * 32 + lrow;
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+          const int wb = wn * 32 + mi * 8;  // first weight row of fragment mi, in 4-row units
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            f32x4_t o;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) o[v] = acc[mi][nj][4 * q + v];
+            const int u = wb + 2 * q + lk;
+            *reinterpret_cast<f32x4_t*>(stg + ts * 1024 + ((u ^ (ts & 15)) << 4)) = o;
+          }
+        }
+      }
+      __syncthreads();
+      const int c = tid & 63;
+#pragma unroll 4
+      for (int ts = tid >> 6; ts < 128; ts += kGemmThreads / 64) {
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stg + ts * 1024 + ((c ^ (ts & 15)) << 4));
+        const int trow = (ts >> 6) * (TM / 2) + 64 * P + (ts & 63);
+        if (trow < trows) *reinterpret_cast<f32x4_t*>(part + (int64_t)trow * 256 + 4 * c) = v;
+      }
+      __syncthreads();
+    }
+  } else if (LAYER == 0) {
     // 256 B per staged row (128 bf16 columns); 8-byte unit u of row t at
     // unit u ^ (t & 31): conflict-free for 32 rows writing the same unit.
     char* stg = lds;

@@ -13,34 +13,130 @@
 
 namespace moe {
 
-// The grid's last round is re-cut: when its r tiles would fill at most half
-// the workgroups, they become 2 r half tiles (128 token rows each), so the
-// round takes about half a tile's time instead of a whole one.  A half tile
-// computes each element exactly as a full tile does (same k order), so the
-// split never changes the result.  (Measured on MI355X: halving the tail
-// tile of every segment instead costs more than the padding it saves.)
+// Workspace of a split last round: header {r, s} and one descriptor
+// {seg_start, seg_rows, m0, nt} per split tile, then the partial
+// accumulators, one 256 x 256 f32 block per unit (at most one unit per CU).
+struct SplitWs {
+  int32_t* hdr;
+  int32_t* desc;
+  float* part;
+};
+constexpr int kMaxSplit = 8;
+constexpr int kMinSplitSteps = 4;  // K steps per range, at least
+constexpr size_t kSplitPartFloats = (size_t)kTileRows * 256;
+constexpr size_t kSplitHdrBytes = 16 + 16 * 4096;  // descriptors of up to 4096 split tiles
+
+// Whether splitting a last-round tile of nk K steps into s ranges shortens
+// the round, in units of one K step of a full tile: the half-tile tail
+// (halfable) takes about 0.55 nk (half the MFMAs, the same operand loads
+// per K step of the weights), an unsplit full tile nk, a split one nk / s
+// plus the partial stores and the reduce pass, about 16 steps (measured on
+// layer 1 with H = 4096: 256 KiB of f32 per unit written, read back once).
+__device__ __forceinline__ bool split_pays(int nk, int s, bool halfable) {
+  const int base = halfable ? 55 * nk : 100 * nk;
+  return base - 100 * nk / s > 1600;
+}
+
+// The grid's last round is re-cut so that it ends sooner.
+//  * Layer 1 with a split workspace (`split` non-null): its r tiles are cut
+//    along K into s = min(grid / r, steps / kMinSplitSteps, kMaxSplit)
+//    ranges each (when split_pays), r s <= grid units, every CU takes at
+//    most one.  A unit stores its raw f32 accumulators (SplitWs::part) and
+//    grouped_gemm_split_reduce adds the s ranges of each tile in increasing
+//    order.  Layer 0 does not split: its tiles are 4 to 7 times shorter, so
+//    the partials and the second pass cost about what the split saves, and
+//    the split path's registers would raise the kernel's spills.
+//  * Otherwise, when its r tiles would fill at most half the workgroups,
+//    they become 2 r half tiles (128 token rows each), which compute each
+//    element exactly as a full tile does.
+// The split is a function of the tile count and the grid, so a given device
+// always splits the same tiles the same way.
 template <int LAYER>
 __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(Bf16GemmArgs args,
                                                                          const int32_t* __restrict__ offsets, int G,
-                                                                         int group_cols) {
+                                                                         int group_cols, SplitWs split) {
   __shared__ __attribute__((aligned(16))) char lds[kGemmLdsBytes];
   __shared__ TileLds tl;
   const int NT = (args.N + (LAYER == 0 ? kL0Cols : kL1Cols) - 1) / (LAYER == 0 ? kL0Cols : kL1Cols);
   const int T = build_tile_table(offsets, G, kTileRows, tl) * NT;
   const int grid = gridDim.x;
   const int r = T % grid;
-  const int split = (r > 0 && 2 * r <= grid && T > grid) ? r : 0;  // tiles of the last round to halve
-  const int entries = T + split;
+  if constexpr (LAYER == 1) {
+    const int nk = args.K / kBK;
+    int s = 1;
+    if (split.hdr && r > 0) s = min(min(grid / r, nk / kMinSplitSteps), kMaxSplit);
+    if (s >= 2 && !split_pays(nk, s, 2 * r <= grid && T > grid)) s = 1;
+    if (split.hdr && blockIdx.x == 0 && threadIdx.x == 0) {
+      split.hdr[0] = s >= 2 ? r : 0;
+      split.hdr[1] = s;
+    }
+    if (s >= 2) {
+      const int tail0 = T - r;
+      const int entries = tail0 + r * s;
+      for (int v = xcd_slot(blockIdx.x, grid); v < entries; v += grid) {
+        if (v < tail0) {
+          const TileCoord c = tile_coord(v, G, NT, kTileRows, group_cols, tl);
+          bf16_gemm_tile<LAYER>(args, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], c.m0, c.nt, lds);
+        } else {
+          const int u = v - tail0, jj = u / s, ck = u - jj * s;
+          const TileCoord c = tile_coord(tail0 + jj, G, NT, kTileRows, group_cols, tl);
+          if (ck == 0 && threadIdx.x == 0) {
+            int32_t* d = split.desc + 4 * jj;
+            d[0] = tl.seg_start[c.g];
+            d[1] = tl.seg_rows[c.g];
+            d[2] = c.m0;
+            d[3] = c.nt;
+          }
+          bf16_gemm_tile<LAYER, false, kTileRows, true>(args, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], c.m0, c.nt,
+                                                        lds, (ck * nk) / s, ((ck + 1) * nk) / s,
+                                                        split.part + (size_t)u * kSplitPartFloats);
+        }
+      }
+      return;
+    }
+  }
+  const int half = (r > 0 && 2 * r <= grid && T > grid) ? r : 0;  // tiles of the last round to halve
+  const int entries = T + half;
   for (int v = xcd_slot(blockIdx.x, grid); v < entries; v += grid) {
-    if (v < T - split) {
+    if (v < T - half) {
       const TileCoord c = tile_coord(v, G, NT, kTileRows, group_cols, tl);
       bf16_gemm_tile<LAYER>(args, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], c.m0, c.nt, lds);
     } else {
-      const int j = v - (T - split);
-      const TileCoord c = tile_coord(T - split + j / 2, G, NT, kTileRows, group_cols, tl);
+      const int j = v - (T - half);
+      const TileCoord c = tile_coord(T - half + j / 2, G, NT, kTileRows, group_cols, tl);
       const int m0 = c.m0 + (j & 1) * (kTileRows / 2);
       if (m0 < tl.seg_rows[c.g]) bf16_gemm_tile<LAYER, false, kTileRows / 2>(args, c.g, tl.seg_start[c.g],
                                                                               tl.seg_rows[c.g], m0, c.nt, lds);
+    }
+  }
+}
+
+// Second pass of a split last round (layer 1): for every split tile, add
+// the partial accumulators of its K ranges in increasing order (f32) and
+// store Y.  Work item = (split tile, 16 token rows); 64 threads per token
+// row, 4 columns each.
+constexpr int kReduceRows = 16;
+
+__global__ __launch_bounds__(256) void grouped_gemm_split_reduce(Bf16GemmArgs args, SplitWs split) {
+  const int r = split.hdr[0], s = split.hdr[1];
+  if (r == 0) return;
+  const int N = args.N;
+  const int items = r * (kTileRows / kReduceRows);
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    const int jj = it / (kTileRows / kReduceRows);
+    const int t0 = (it % (kTileRows / kReduceRows)) * kReduceRows;
+    const int32_t* d = split.desc + 4 * jj;
+    const int seg_start = d[0], seg_rows = d[1], m0 = d[2], nt = d[3];
+    const float* base = split.part + (size_t)jj * s * kSplitPartFloats;
+    const int c = threadIdx.x & 63;
+    const int n = nt * kL1Cols + 4 * c;
+    for (int t = t0 + (threadIdx.x >> 6); t < t0 + kReduceRows; t += 4) {
+      const int trow = m0 + t;
+      if (trow >= seg_rows || n >= N) continue;
+      f32x4_t ys = {0.f, 0.f, 0.f, 0.f};
+      for (int k = 0; k < s; ++k)
+        ys += *reinterpret_cast<const f32x4_t*>(base + (size_t)k * kSplitPartFloats + (size_t)t * 256 + 4 * c);
+      *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(args.c) + (int64_t)(seg_start + trow) * N + n) = ys;
     }
   }
 }
@@ -139,6 +235,11 @@ int device_cu_count() {
   return g_cu_count;
 }
 
+size_t gemm_split_ws_bytes() {
+  const size_t units = (size_t)device_cu_count();
+  return kSplitHdrBytes + units * kSplitPartFloats * sizeof(float);
+}
+
 hipError_t launch_grouped_gemm_bf16(const GemmProblem& gp, hipStream_t s) {
   if (gp.R == 0) return hipSuccess;
   Bf16GemmArgs a;
@@ -154,10 +255,21 @@ hipError_t launch_grouped_gemm_bf16(const GemmProblem& gp, hipStream_t s) {
   a.M = 0;
   const int grid = device_cu_count();
   const int group_cols = grid / kXcds > 0 ? grid / kXcds : 1;
+  SplitWs sp{nullptr, nullptr, nullptr};
+  // layer 1 only; the header holds descriptors of up to 4096 split tiles (fewer than the grid)
+  if (gp.layer == 1 && gp.ws && gp.ws_bytes >= gemm_split_ws_bytes() && grid <= 4096) {
+    char* w = reinterpret_cast<char*>(gp.ws);
+    sp.hdr = reinterpret_cast<int32_t*>(w);
+    sp.desc = sp.hdr + 4;
+    sp.part = reinterpret_cast<float*>(w + kSplitHdrBytes);
+  }
   if (gp.layer == 0)
-    grouped_gemm_bf16_kernel<0><<<grid, kGemmThreads, 0, s>>>(a, gp.offsets, gp.G, group_cols);
+    grouped_gemm_bf16_kernel<0><<<grid, kGemmThreads, 0, s>>>(a, gp.offsets, gp.G, group_cols, sp);
   else
-    grouped_gemm_bf16_kernel<1><<<grid, kGemmThreads, 0, s>>>(a, gp.offsets, gp.G, group_cols);
+    grouped_gemm_bf16_kernel<1><<<grid, kGemmThreads, 0, s>>>(a, gp.offsets, gp.G, group_cols, sp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !sp.hdr) return e;
+  grouped_gemm_split_reduce<<<grid, 256, 0, s>>>(a, sp);
   return hipGetLastError();
 }
 

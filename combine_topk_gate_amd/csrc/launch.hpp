@@ -39,7 +39,11 @@ struct GemmProblem {
   int N;  // output columns: F (layer 0) or H (layer 1)
   int E;
   int G;
+  void* ws = nullptr;       // bf16: split workspace of gemm_split_ws_bytes(), or null
+  size_t ws_bytes = 0;
 };
+// Workspace that lets the bf16 grouped GEMM split its last round along K.
+size_t gemm_split_ws_bytes();
 hipError_t launch_grouped_gemm_bf16(const GemmProblem& gp, hipStream_t s);
 hipError_t launch_grouped_gemm_f32(const GemmProblem& gp, hipStream_t s);
 

@@ -136,7 +136,17 @@ moe_status_t moe_dispatch(const moe_problem_t* p, const void* x, const int32_t* 
  *     a  = Hact [R,F] dtype; w0 = W_down [E,H,F]; w1 = NULL
  *     c  = Y [R,H] f32: Y[r,n] = sum_f Hact[r,f] W_down[e,n,f], f32 accumulation.
  *   offsets [G+1] int32 as produced by moe_dispatch.  Rows of empty segments
- *   produce nothing.  ws may be NULL (moe_workspace_bytes returns 0).
+ *   produce nothing.
+ *   ws (bf16 layers): NULL, or at least moe_workspace_bytes(p,
+ *   MOE_OP_GROUPED_GEMM) bytes, 16-byte aligned (a misaligned ws returns
+ *   MOE_ERR_INVALID_ARGUMENT).  Layer 1 with it computes the tiles of the
+ *   persistent grid's last round in up to 8 ranges of k ([GGEMM] tile
+ *   scheduling over uneven problems) whose f32 partial sums a second pass
+ *   adds in increasing k order, so the last round ends sooner; without it
+ *   (or when smaller), and always in layer 0, those tiles are cut into half
+ *   tiles instead.  Every product is still accumulated in f32; only the
+ *   grouping of the k sum of those tiles differs, and a given device always
+ *   splits the same tiles.  f32 layers use no workspace.
  */
 moe_status_t moe_grouped_gemm(const moe_problem_t* p, int32_t layer, const void* a, const void* w0, const void* w1,
                               const int32_t* offsets, void* c, void* ws, size_t ws_bytes, void* stream);
@@ -188,7 +198,10 @@ typedef struct {
  * dedicated workgroups or in the shared queue.  Counters in the workspace
  * are the ready flags.  f32 layers, and opts->fused == 0, run the kernel
  * chain moe_route -> moe_dispatch -> moe_grouped_gemm(0) ->
- * moe_grouped_gemm(1) -> moe_combine instead; both paths give the same bits.
+ * moe_grouped_gemm(1) -> moe_combine instead.  The fused kernel gives the
+ * same bits as that chain run without a grouped-GEMM workspace; moe_layer's
+ * own chain passes one (the last round split along k, see
+ * moe_grouped_gemm), which regroups the k sum of those tiles only.
  *   x [M,H] dtype; logits [M,E] f32; src_block [M] int32 or NULL (S = 1);
  *   w_gate, w_up [E,F,H]; w_down [E,H,F]; out [M,H] f32.
  *   aux: the fused path writes X_perm only if aux->x_perm is given.

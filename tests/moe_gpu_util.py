@@ -33,9 +33,12 @@ def upload(d, device="cuda:0"):
     return {k: dev(v, device) for k, v in d.items()}
 
 
-def run_chain(cfg, g, device="cuda:0"):
+def run_chain(cfg, g, device="cuda:0", gemm_ws=True):
     """moe_route -> moe_dispatch -> moe_grouped_gemm(0) -> (1) -> moe_combine.
-    g: dict of device tensors x, logits, src_block, w_gate, w_up, w_down."""
+    g: dict of device tensors x, logits, src_block, w_gate, w_up, w_down.
+    gemm_ws: give the grouped GEMM its workspace (the grid's last round is
+    then split along k, as in moe_layer's chain); without it the GEMM runs
+    unsplit, which is what the fused kernel reproduces bit for bit."""
     p = problem_of(cfg)
     M, k, H, F, G, R = cfg.M, cfg.k, cfg.H, cfg.F, cfg.S * cfg.E, cfg.M * cfg.k
     act = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
@@ -55,11 +58,20 @@ def run_chain(cfg, g, device="cuda:0"):
     moe.moe_route(p, g["logits"], o["topk_idx"], o["topk_w"])
     moe.moe_dispatch(p, g["x"], o["topk_idx"], g.get("src_block"), o["counts"], o["offsets"], o["sorted_to_flat"],
                      o["flat_to_sorted"], o["x_perm"], ws)
-    moe.moe_grouped_gemm(p, 0, o["x_perm"], g["w_gate"], g["w_up"], o["offsets"], o["hact"])
-    moe.moe_grouped_gemm(p, 1, o["hact"], g["w_down"], None, o["offsets"], o["y"])
+    gws = None
+    nws = moe.moe_workspace_bytes(p, moe.MOE_OP_GROUPED_GEMM)
+    if gemm_ws and nws > 0:
+        gws = torch.empty(nws, dtype=torch.uint8, device=device)
+    moe.moe_grouped_gemm(p, 0, o["x_perm"], g["w_gate"], g["w_up"], o["offsets"], o["hact"], gws)
+    moe.moe_grouped_gemm(p, 1, o["hact"], g["w_down"], None, o["offsets"], o["y"], gws)
     moe.moe_combine(p, o["y"], o["topk_w"], o["flat_to_sorted"], o["out"])
     torch.cuda.synchronize()
     return o
+
+
+def layer_runs_chain(cfg):
+    """True if moe_layer's default plan for cfg is the kernel chain."""
+    return cfg.dtype != "bf16" or moe.moe_layer_default_movers(problem_of(cfg)) < 0
 
 
 def run_layer(cfg, g, device="cuda:0", aux=False, **opts):

@@ -12,15 +12,16 @@ import torch
 
 import combine_topk_gate_amd as moe
 import moe_synth
-from moe_gpu_util import run_chain, run_layer, upload
+from moe_gpu_util import layer_runs_chain, run_chain, run_layer, upload
 
 pytestmark = pytest.mark.gpu
 
 
 def _case(cfg):
+    # the fused kernel reproduces the unsplit chain (no grouped-GEMM workspace)
     d = moe_synth.make_inputs(cfg)
     g = upload(d)
-    return cfg, g, run_chain(cfg, g)
+    return cfg, g, run_chain(cfg, g, gemm_ws=False)
 
 
 @pytest.fixture(scope="module")
@@ -66,6 +67,9 @@ def test_source_blocks(ep, n_mover):
 
 def test_intermediates_equal_chain(qwen):
     cfg, g, chain = qwen
+    if layer_runs_chain(cfg):
+        # the default options run the kernel chain, whose GEMM splits the last round
+        chain = run_chain(cfg, g, gemm_ws=True)
     out, aux, status = run_layer(cfg, g, aux=True)
     assert status == moe.MOE_OK
     for key in ("topk_idx", "topk_w", "counts", "offsets", "sorted_to_flat", "flat_to_sorted", "y"):
@@ -76,7 +80,9 @@ def test_intermediates_equal_chain(qwen):
 
 
 def test_unfused_option_equals_chain(qwen):
-    cfg, g, chain = qwen
+    # moe_layer's chain gives its grouped GEMM the workspace (split last round)
+    cfg, g, _ = qwen
+    chain = run_chain(cfg, g, gemm_ws=True)
     out, _, status = run_layer(cfg, g, fused=0)
     assert status == moe.MOE_OK
     assert torch.equal(out, chain["out"])

@@ -18,7 +18,7 @@ import torch
 
 import moe_synth
 import oracle
-from moe_gpu_util import dev, host, rel_fro, run_chain, run_layer, tolerances, upload
+from moe_gpu_util import dev, host, layer_runs_chain, rel_fro, run_chain, run_layer, tolerances, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -121,7 +121,58 @@ def test_layer_equals_chain_bitwise(case):
     c = case
     out, _, status = run_layer(c["cfg"], c["g"])
     assert status == 0
-    assert torch.equal(out, c["out"]["out"])
+    ref = c["out"] if layer_runs_chain(c["cfg"]) else run_chain(c["cfg"], c["g"], gemm_ws=False)
+    assert torch.equal(out, ref["out"])
+
+
+def _check_against_exact(cfg, g, chain, elems, hacts):
+    """Each Hact value at (row, col) in elems lies within bf16 rounding plus
+    an f32 accumulation allowance of the exact f64 value: gate and up are
+    recomputed from the bf16 operands, and the allowance is 8 f32 ulps of
+    the sums of absolute terms, carried through SwiGLU's partial
+    derivatives."""
+    if not elems:
+        return
+    offs = chain["offsets"].cpu().numpy()
+    u = 2.0 ** -24
+    for r, col in elems:
+        grp = int(np.searchsorted(offs, r, side="right") - 1)
+        e = grp % cfg.E
+        x = chain["x_perm"][r].double().cpu()
+        wg = g["w_gate"][e, col].double().cpu()
+        wu = g["w_up"][e, col].double().cpu()
+        gv, uv = float(x @ wg), float(x @ wu)
+        sg, su = float(x.abs() @ wg.abs()), float(x.abs() @ wu.abs())
+        sig = 1.0 / (1.0 + np.exp(-gv))
+        silu, dsilu = gv * sig, sig * (1.0 + gv * (1.0 - sig))
+        exact = silu * uv
+        allow = 2.0 ** -8 * abs(exact) + 8 * u * (abs(silu) * su + abs(dsilu * uv) * sg) + 1e-12
+        for h in hacts:
+            assert abs(float(h[r, col]) - exact) <= allow, (r, col, float(h[r, col]), exact, allow)
+
+
+def test_split_last_round_matches_unsplit(case):
+    """The grouped GEMM with its workspace (last round split along k) against
+    the same GEMM without it: identical routing and Hact/Y within f32
+    regrouping error; and the split path is deterministic."""
+    c = case
+    if c["cfg"].dtype != "bf16":
+        pytest.skip("f32 layers do not split")
+    un = run_chain(c["cfg"], c["g"], gemm_ws=False)
+    again = run_chain(c["cfg"], c["g"], gemm_ws=True)
+    for key in ("hact", "y", "out"):
+        assert torch.equal(again[key], c["out"][key]), key
+    y0, y1 = un["y"].double(), c["out"]["y"].double()
+    assert float((y1 - y0).norm() / y0.norm()) <= 1e-5
+    h0, h1 = un["hact"].double(), c["out"]["hact"].double()
+    # a regrouped f32 sum may cross a bf16 rounding boundary: one step at most,
+    # unless the gate or up sum cancels (|sum| << sum of |terms|); such
+    # elements are checked against the exact f64 value instead
+    far = ((h1 - h0).abs() > 2.0 ** -7 * h0.abs() + 1e-6).nonzero().tolist()
+    assert len(far) <= 64, len(far)
+    _check_against_exact(c["cfg"], c["g"], un, far, [h0, h1])
+    o0, o1 = un["out"].double(), c["out"]["out"].double()
+    assert float((o1 - o0).norm() / o0.norm()) <= 1e-4
 
 
 # ------------------------------------------------------------ edge cases --
@@ -144,7 +195,12 @@ EDGE = {
     "src_blocks_empty_segment": dict(M=256, H=128, F=128, E=4, k=2, S=8, bias=[0, 0, 0, -60]),
     "f32_ragged": dict(M=77, H=64, F=192, E=5, k=3, dtype="f32"),
     "k16_E64": dict(M=40, H=64, F=64, E=64, k=16),
+    # one partial round of layer-1 tiles, split 8 ways along F (36 steps: uneven ranges)
+    "split_single_round": dict(M=300, H=512, F=2304, E=4, k=2),
+    # ... with empty experts and ragged segments (50 steps)
+    "split_empty_experts": dict(M=200, H=256, F=3200, E=8, k=2, bias=[4, 4, 0, 0, -50, -50, 0, -50]),
 }
+SPLIT_EDGES = ["split_single_round", "split_empty_experts"]
 
 
 @pytest.mark.parametrize("edge", list(EDGE))
@@ -164,7 +220,26 @@ def test_edge_case_full_parity(edge):
     if mabs is not None:
         assert np.max(np.abs(host(o["out"]) - r["out"])) <= mabs
     out, _, status = run_layer(cfg, g)
-    assert status == 0 and torch.equal(out, o["out"])
+    ref = o if layer_runs_chain(cfg) else run_chain(cfg, g, gemm_ws=False)
+    assert status == 0 and torch.equal(out, ref["out"])
+
+
+@pytest.mark.parametrize("edge", SPLIT_EDGES)
+def test_split_path_runs_and_is_deterministic(edge):
+    """These shapes take the layer-1 split (a grid of one partial round, long
+    F): its Y differs in rounding from the unsplit GEMM (so the split ran),
+    stays within f32 regrouping error of it, and repeats bit for bit."""
+    kw = dict(EDGE[edge])
+    bias = kw.pop("bias", None)
+    cfg, d = _edge_inputs(**kw, bias=bias)
+    g = upload(d)
+    a, b = run_chain(cfg, g), run_chain(cfg, g)
+    un = run_chain(cfg, g, gemm_ws=False)
+    assert torch.equal(a["y"], b["y"]) and torch.equal(a["out"], b["out"])
+    assert torch.equal(a["hact"].view(torch.int16), un["hact"].view(torch.int16))  # layer 0 never splits
+    assert not torch.equal(a["y"], un["y"])
+    y0, y1 = un["y"].double(), a["y"].double()
+    assert float((y1 - y0).norm() / y0.norm()) <= 1e-5
 
 
 def test_zero_tokens_is_a_no_op():

@@ -43,16 +43,17 @@ def _configure(lib):
     lib.orc_round_to_bf16.argtypes = [ctypes.c_double]
     lib.orc_round_to_bf16.restype = ctypes.c_double
     lib.orc_route.argtypes = [I64, I32, I32, P, P, P]
-    lib.orc_counts_offsets.argtypes = [I64, I32, I32, I32, P, P, P, P]
-    lib.orc_permutation.argtypes = [I64, I32, I32, I32, P, P, P, P]
+    lib.orc_counts_offsets.argtypes = [I64, I32, I32, I32, I32, I32, P, P, P, P]
+    lib.orc_permutation.argtypes = [I64, I32, I32, I32, I32, I32, P, P, P, P]
     lib.orc_dispatch.argtypes = [I64, I32, I32, I32, P, P, P]
     lib.orc_ffn_rows.argtypes = [I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, I64, P, P, P]
-    lib.orc_combine_tokens.argtypes = [I32, I32, I64, P, P, P]
-    lib.orc_moe_layer.argtypes = [I64, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, I64, P,
+    lib.orc_combine_tokens.argtypes = [I32, I32, I64, P, P, P, P]
+    lib.orc_epilogue.argtypes = [I64, P, P, I32, I32, P]
+    lib.orc_moe_layer.argtypes = [I64, I32, I32, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, I64, P,
                                   P, P, P, P, P, P, P, P, P]
     lib.orc_num_threads.argtypes = []
     for name in ("orc_route", "orc_counts_offsets", "orc_permutation", "orc_dispatch",
-                 "orc_ffn_rows", "orc_combine_tokens", "orc_moe_layer", "orc_num_threads"):
+                 "orc_ffn_rows", "orc_combine_tokens", "orc_epilogue", "orc_moe_layer", "orc_num_threads"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -140,26 +141,35 @@ def route(logits, k):
     return idx, w
 
 
-def counts_offsets(topk_idx, E, S=1, src_block=None):
-    """Step 2: per-(source block, expert) counts and the exclusive prefix sum."""
+def _local(E, expert_base, local_experts):
+    return local_experts if local_experts else E
+
+
+def counts_offsets(topk_idx, E, S=1, src_block=None, expert_base=0, local_experts=0):
+    """Step 2: per-(source block, expert) counts and the exclusive prefix sum.
+    With local_experts = EL > 0 only pairs routed to experts
+    [expert_base, expert_base + EL) are counted, as segment src*EL + (e - base)."""
     topk_idx = _c(topk_idx, np.int32)
     src_block = _c(src_block, np.int32)
     M, k = topk_idx.shape
-    counts = np.empty(S * E, np.int32)
-    offsets = np.empty(S * E + 1, np.int32)
-    _check(_load().orc_counts_offsets(M, E, k, S, _p(topk_idx), _p(src_block), _p(counts), _p(offsets)),
-           "counts_offsets")
+    G = S * _local(E, expert_base, local_experts)
+    counts = np.empty(G, np.int32)
+    offsets = np.empty(G + 1, np.int32)
+    _check(_load().orc_counts_offsets(M, E, k, S, expert_base, local_experts, _p(topk_idx), _p(src_block),
+                                      _p(counts), _p(offsets)), "counts_offsets")
     return counts, offsets
 
 
-def permutation(topk_idx, E, S=1, src_block=None):
-    """Step 3: the stable permutation and its inverse."""
+def permutation(topk_idx, E, S=1, src_block=None, expert_base=0, local_experts=0):
+    """Step 3: the stable permutation and its inverse (-1 for dropped pairs
+    and for sorted positions past the kept pairs)."""
     topk_idx = _c(topk_idx, np.int32)
     src_block = _c(src_block, np.int32)
     M, k = topk_idx.shape
     s2f = np.empty(M * k, np.int32)
     f2s = np.empty(M * k, np.int32)
-    _check(_load().orc_permutation(M, E, k, S, _p(topk_idx), _p(src_block), _p(s2f), _p(f2s)), "permutation")
+    _check(_load().orc_permutation(M, E, k, S, expert_base, local_experts, _p(topk_idx), _p(src_block), _p(s2f),
+                                   _p(f2s)), "permutation")
     return s2f, f2s
 
 
@@ -189,43 +199,75 @@ def ffn_rows(x, w_gate, w_up, w_down, k, S, sorted_to_flat, offsets, rows):
     return hact, y
 
 
-def combine_tokens(topk_w_sub, y_rows):
-    """Step 7: out[i] = sum_j w[i,j] * y_rows[i*k+j] in float64."""
+def combine_tokens(topk_w_sub, y_rows, kept=None):
+    """Step 7: out[i] = sum over kept j of w[i,j] * y_rows[i*k+j] in float64
+    (kept [n,k] bool, None: every pair)."""
     w = _c(topk_w_sub, np.float32)
     n, k = w.shape
     y_rows = _c(y_rows, np.float64)
     H = y_rows.shape[1]
+    kp = None if kept is None else _c(np.asarray(kept, bool).astype(np.uint8), np.uint8)
     out = np.empty((n, H), np.float64)
-    _check(_load().orc_combine_tokens(H, k, n, _p(w), _p(y_rows), _p(out)), "combine_tokens")
+    _check(_load().orc_combine_tokens(H, k, n, _p(w), _p(y_rows), _p(kp), _p(out)), "combine_tokens")
     return out
 
 
-def moe_layer(x, logits, w_gate, w_up, w_down, k, S=1, src_block=None, tokens=None, want_rows=False):
+def epilogue(acc, residual=None, out_dtype="f32"):
+    """cast(acc + residual): the residual (f32 array, or uint16 bf16 bits)
+    widened exactly, the sum in float64, rounded to bf16 (nearest even) when
+    out_dtype is "bf16".  Returns float64 values."""
+    acc = _c(acc, np.float64)
+    res = None if residual is None else np.ascontiguousarray(residual)
+    if res is not None:
+        assert res.shape == acc.shape
+    rdt = F32 if res is None else _dtype_code(res)
+    odt = {"f32": F32, "bf16": BF16}[out_dtype]
+    out = np.empty(acc.shape, np.float64)
+    _check(_load().orc_epilogue(acc.size, _p(acc), _p(res), rdt, odt, _p(out)), "epilogue")
+    return out
+
+
+def moe_layer(x, logits, w_gate, w_up, w_down, k, S=1, src_block=None, tokens=None, want_rows=False,
+              expert_base=0, local_experts=0, residual=None, out_dtype="f32"):
     """The whole layer.  Routing, counts, offsets and the permutation are
     computed for every token; the FFN and the combine for ``tokens`` only
-    (all tokens if None).  Returns a dict of numpy arrays."""
+    (all tokens if None).  Routing chooses among logits.shape[1] experts;
+    with local_experts = EL > 0 the weights hold experts
+    [expert_base, expert_base + EL) only and out is the partial combine over
+    the pairs routed to them.  residual [M,H] and out_dtype select the
+    epilogue cast(acc + residual) ("out" then holds its values; "acc" the
+    plain combine).  Returns a dict of numpy arrays."""
     x = np.ascontiguousarray(x)
     dt = _dtype_code(x)
     logits = _c(logits, np.float32)
     M, H = x.shape
-    E, F, H2 = w_gate.shape
+    EL, F, H2 = w_gate.shape
+    E = logits.shape[1]
     assert H2 == H and logits.shape == (M, E)
+    assert EL == _local(E, expert_base, local_experts)
     wg, wu, wd = (np.ascontiguousarray(a, dtype=x.dtype) for a in (w_gate, w_up, w_down))
     src_block = _c(src_block, np.int32)
     tok = None if tokens is None else _c(tokens, np.int64)
     n_tok = M if tok is None else tok.shape[0]
     r = dict(
         topk_idx=np.empty((M, k), np.int32), topk_w=np.empty((M, k), np.float32),
-        counts=np.empty(S * E, np.int32), offsets=np.empty(S * E + 1, np.int32),
+        counts=np.empty(S * EL, np.int32), offsets=np.empty(S * EL + 1, np.int32),
         sorted_to_flat=np.empty(M * k, np.int32), flat_to_sorted=np.empty(M * k, np.int32),
         out=np.empty((n_tok, H), np.float64))
     hact = np.empty((n_tok * k, F), np.float64) if want_rows else None
     y = np.empty((n_tok * k, H), np.float64) if want_rows else None
-    _check(_load().orc_moe_layer(M, H, F, E, k, S, dt, _p(x), _p(logits), _p(src_block), _p(wg), _p(wu), _p(wd),
-                                 n_tok, _p(tok), _p(r["topk_idx"]), _p(r["topk_w"]), _p(r["counts"]),
-                                 _p(r["offsets"]), _p(r["sorted_to_flat"]), _p(r["flat_to_sorted"]),
-                                 _p(r["out"]), _p(hact), _p(y)), "moe_layer")
+    _check(_load().orc_moe_layer(M, H, F, E, k, S, expert_base, local_experts, dt, _p(x), _p(logits),
+                                 _p(src_block), _p(wg), _p(wu), _p(wd), n_tok, _p(tok), _p(r["topk_idx"]),
+                                 _p(r["topk_w"]), _p(r["counts"]), _p(r["offsets"]), _p(r["sorted_to_flat"]),
+                                 _p(r["flat_to_sorted"]), _p(r["out"]), _p(hact), _p(y)), "moe_layer")
     if want_rows:
         r["hact"] = hact
         r["y"] = y
+    if residual is not None or out_dtype != "f32":
+        r["acc"] = r["out"]
+        res = None
+        if residual is not None:
+            res = np.ascontiguousarray(residual)
+            res = res if tokens is None else res[tok]
+        r["out"] = epilogue(r["acc"], res, out_dtype)
     return r

@@ -29,6 +29,20 @@
  *   combine  -> out[t] = sum_j w[t,j] * Y[flat_to_sorted[t*k+j]], summed from
  *               zero in slot order j = 0..k-1 (COMET review §4.1.1 Top-K
  *               reduction; PTO MoE article "Combine / Unpermute").
+ *   epilogue -> out = cast(acc + residual) (grouped-GEMM article, fused
+ *               GemmAdd epilogue: the accumulator plus an added tensor,
+ *               then the cast to the output type), bf16 by round to
+ *               nearest even.
+ *
+ * Local experts (expert parallelism, COMET review §4.1.2 and the PTO MoE
+ * article's measured case of 16 local experts per card): routing chooses
+ * among all E experts, and a call that holds only experts
+ * [base, base + EL) keeps the pairs routed to them.  Kept pair f goes to
+ * segment src * EL + (expert - base); the other pairs are dropped: they get
+ * no sorted position (flat_to_sorted[f] = -1), sorted positions past the
+ * kept ones hold -1, and the combine leaves them out, so out is this
+ * call's share of the token's sum (the partial combine that the other
+ * holders of experts complete).  EL = E, base = 0 is the plain layer.
  *
  * Storage conventions (shared with the library's public header by
  * specification only, not by code):
@@ -135,50 +149,74 @@ int orc_route(int64_t M, int E, int k, const float* logits, int32_t* topk_idx, f
 
 /* ------------------------------------------------------------ segments --- */
 
-static int64_t seg_of(const int32_t* topk_idx, const int32_t* src_block, int E, int k, int64_t f) {
-  int64_t t = f / k;
-  int64_t s = src_block ? (int64_t)src_block[t] : 0;
-  return s * E + topk_idx[f];
+/* Number of experts this call holds: EL, or all E when EL is 0. */
+static int local_count(int E, int EL) { return EL > 0 ? EL : E; }
+
+static int valid_local(int E, int base, int EL) {
+  return base >= 0 && EL >= 0 && (EL == 0 ? base == 0 : base + EL <= E);
 }
 
-/* counts[g] = number of pairs in segment g = src*E + expert; offsets = exclusive prefix sum. */
-int orc_counts_offsets(int64_t M, int E, int k, int S, const int32_t* topk_idx, const int32_t* src_block,
-                       int32_t* counts, int32_t* offsets) {
-  if (M < 0 || E < 1 || k < 1 || S < 1) return ORC_EINVAL;
-  int64_t G = (int64_t)S * E, R = M * k;
+/* Segment of pair f: src * EL + (expert - base), or -1 if its expert is not
+ * held here. */
+static int64_t seg_of(const int32_t* topk_idx, const int32_t* src_block, int base, int EL, int k, int64_t f) {
+  int64_t t = f / k;
+  int64_t s = src_block ? (int64_t)src_block[t] : 0;
+  int64_t e = (int64_t)topk_idx[f] - base;
+  if (e < 0 || e >= EL) return -1;
+  return s * EL + e;
+}
+
+/* counts[g] = number of kept pairs in segment g = src*EL + (expert - base);
+ * offsets = exclusive prefix sum (offsets[G] = number of kept pairs). */
+int orc_counts_offsets(int64_t M, int E, int k, int S, int base, int EL, const int32_t* topk_idx,
+                       const int32_t* src_block, int32_t* counts, int32_t* offsets) {
+  if (M < 0 || E < 1 || k < 1 || S < 1 || !valid_local(E, base, EL)) return ORC_EINVAL;
+  EL = local_count(E, EL);
+  int64_t G = (int64_t)S * EL, R = M * k;
   for (int64_t g = 0; g < G; ++g) counts[g] = 0;
   for (int64_t f = 0; f < R; ++f) {
-    int64_t g = seg_of(topk_idx, src_block, E, k, f);
-    if (g < 0 || g >= G) return ORC_EINVAL;
-    counts[g] += 1;
+    if (topk_idx[f] < 0 || topk_idx[f] >= E) return ORC_EINVAL;
+    int64_t g = seg_of(topk_idx, src_block, base, EL, k, f);
+    if (g >= G) return ORC_EINVAL;
+    if (g >= 0) counts[g] += 1;
   }
   offsets[0] = 0;
   for (int64_t g = 0; g < G; ++g) offsets[g + 1] = offsets[g] + counts[g];
   return ORC_OK;
 }
 
-/* Segment by segment, every pair of that segment in increasing flat index. */
-int orc_permutation(int64_t M, int E, int k, int S, const int32_t* topk_idx, const int32_t* src_block,
-                    int32_t* sorted_to_flat, int32_t* flat_to_sorted) {
-  if (M < 0 || E < 1 || k < 1 || S < 1) return ORC_EINVAL;
-  int64_t G = (int64_t)S * E, R = M * k, r = 0;
+/* Segment by segment, every kept pair of that segment in increasing flat
+ * index; sorted positions past the kept pairs and flat_to_sorted of the
+ * dropped pairs hold -1. */
+int orc_permutation(int64_t M, int E, int k, int S, int base, int EL, const int32_t* topk_idx,
+                    const int32_t* src_block, int32_t* sorted_to_flat, int32_t* flat_to_sorted) {
+  if (M < 0 || E < 1 || k < 1 || S < 1 || !valid_local(E, base, EL)) return ORC_EINVAL;
+  EL = local_count(E, EL);
+  int64_t G = (int64_t)S * EL, R = M * k, r = 0;
   for (int64_t g = 0; g < G; ++g)
     for (int64_t f = 0; f < R; ++f)
-      if (seg_of(topk_idx, src_block, E, k, f) == g) sorted_to_flat[r++] = (int32_t)f;
-  if (r != R) return ORC_EINVAL;
-  for (int64_t q = 0; q < R; ++q) flat_to_sorted[sorted_to_flat[q]] = (int32_t)q;
+      if (seg_of(topk_idx, src_block, base, EL, k, f) == g) sorted_to_flat[r++] = (int32_t)f;
+  int64_t kept = r;
+  for (; r < R; ++r) sorted_to_flat[r] = -1;
+  for (int64_t f = 0; f < R; ++f) flat_to_sorted[f] = -1;
+  for (int64_t q = 0; q < kept; ++q) flat_to_sorted[sorted_to_flat[q]] = (int32_t)q;
   return ORC_OK;
 }
 
 /* ------------------------------------------------------------ dispatch --- */
 
-/* X_perm[r, :] = x[sorted_to_flat[r] / k, :], a byte copy of the token row. */
+/* X_perm[r, :] = x[sorted_to_flat[r] / k, :], a byte copy of the token row;
+ * rows whose sorted position holds no pair (-1) are left zero. */
 int orc_dispatch(int64_t M, int H, int k, int elem_bytes, const void* x, const int32_t* sorted_to_flat,
                  void* x_perm) {
   if (M < 0 || H < 1 || k < 1 || (elem_bytes != 2 && elem_bytes != 4)) return ORC_EINVAL;
   int64_t R = M * k;
   size_t row = (size_t)H * (size_t)elem_bytes;
   for (int64_t r = 0; r < R; ++r) {
+    if (sorted_to_flat[r] < 0) {
+      memset((char*)x_perm + (size_t)r * row, 0, row);
+      continue;
+    }
     int64_t t = sorted_to_flat[r] / k;
     memcpy((char*)x_perm + (size_t)r * row, (const char*)x + (size_t)t * row, row);
   }
@@ -224,7 +262,8 @@ static int64_t segment_of_row(const int32_t* offsets, int64_t G, int64_t r) {
 
 /*
  * Layer0 + Layer1 for a list of sorted rows.  Row r belongs to segment g and
- * uses expert g % E; its input is X_perm[r] = x[sorted_to_flat[r] / k].
+ * uses expert g % E of the weights given (E = the experts held here); its
+ * input is X_perm[r] = x[sorted_to_flat[r] / k].
  * hact_out [n_rows, F] and y_out [n_rows, H] in double (either may be NULL).
  */
 int orc_ffn_rows(int H, int F, int E, int S, int k, int dtype, const void* x, const void* w_gate,
@@ -258,16 +297,37 @@ int orc_ffn_rows(int H, int F, int E, int S, int k, int dtype, const void* x, co
  * out[i, :] = sum_{j=0..k-1} w[t,j] * Y[flat_to_sorted[t*k+j], :] for the
  * listed tokens t = tokens[i]; y_rows supplies Y for the pairs of those
  * tokens, in (i, j) order: y_rows[(i*k + j), :] is the row of pair t*k+j.
+ * kept (may be NULL: all kept) marks the pairs held here; the others are
+ * left out of the sum.
  */
-int orc_combine_tokens(int H, int k, int64_t n_tok, const float* topk_w_sub, const double* y_rows, double* out) {
+int orc_combine_tokens(int H, int k, int64_t n_tok, const float* topk_w_sub, const double* y_rows,
+                       const uint8_t* kept, double* out) {
   if (H < 1 || k < 1) return ORC_EINVAL;
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n_tok; ++i) {
     for (int n = 0; n < H; ++n) {
       double acc = 0.0;
-      for (int j = 0; j < k; ++j) acc += (double)topk_w_sub[i * k + j] * y_rows[(i * k + j) * H + n];
+      for (int j = 0; j < k; ++j)
+        if (!kept || kept[i * k + j]) acc += (double)topk_w_sub[i * k + j] * y_rows[(i * k + j) * H + n];
       out[i * H + n] = acc;
     }
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------- epilogue --- */
+
+/*
+ * out[i] = cast(acc[i] + residual[i]) for n values: the residual (NULL: none)
+ * widened exactly from res_dtype, the sum in double, then rounded to bf16
+ * (round to nearest even) when out_dtype is bf16, else kept.
+ */
+int orc_epilogue(int64_t n, const double* acc, const void* residual, int res_dtype, int out_dtype, double* out) {
+  if (n < 0 || (res_dtype != ORC_F32 && res_dtype != ORC_BF16) || (out_dtype != ORC_F32 && out_dtype != ORC_BF16))
+    return ORC_EINVAL;
+  for (int64_t i = 0; i < n; ++i) {
+    double v = acc[i] + (residual ? load_elem(residual, res_dtype, i) : 0.0);
+    out[i] = (out_dtype == ORC_BF16) ? orc_round_to_bf16(v) : v;
   }
   return ORC_OK;
 }
@@ -284,37 +344,63 @@ int orc_combine_tokens(int H, int k, int64_t n_tok, const float* topk_w_sub, con
  * hact [n_tok*k, F] and y [n_tok*k, H] double (may be NULL), row i*k+j
  * belongs to pair (tokens[i], j).
  */
-int orc_moe_layer(int64_t M, int H, int F, int E, int k, int S, int dtype, const void* x, const float* logits,
-                  const int32_t* src_block, const void* w_gate, const void* w_up, const void* w_down,
-                  int64_t n_tok, const int64_t* tokens, int32_t* topk_idx, float* topk_w, int32_t* counts,
-                  int32_t* offsets, int32_t* sorted_to_flat, int32_t* flat_to_sorted, double* out, double* hact,
-                  double* y) {
+int orc_moe_layer(int64_t M, int H, int F, int E, int k, int S, int base, int EL, int dtype, const void* x,
+                  const float* logits, const int32_t* src_block, const void* w_gate, const void* w_up,
+                  const void* w_down, int64_t n_tok, const int64_t* tokens, int32_t* topk_idx, float* topk_w,
+                  int32_t* counts, int32_t* offsets, int32_t* sorted_to_flat, int32_t* flat_to_sorted, double* out,
+                  double* hact, double* y) {
   int rc = orc_route(M, E, k, logits, topk_idx, topk_w);
   if (rc) return rc;
-  rc = orc_counts_offsets(M, E, k, S, topk_idx, src_block, counts, offsets);
+  rc = orc_counts_offsets(M, E, k, S, base, EL, topk_idx, src_block, counts, offsets);
   if (rc) return rc;
-  rc = orc_permutation(M, E, k, S, topk_idx, src_block, sorted_to_flat, flat_to_sorted);
+  rc = orc_permutation(M, E, k, S, base, EL, topk_idx, src_block, sorted_to_flat, flat_to_sorted);
   if (rc) return rc;
   if (!tokens && n_tok != M) return ORC_EINVAL;
+  EL = local_count(E, EL);
 
   int64_t n_pairs = n_tok * k;
   int64_t* rows = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n_pairs > 0 ? n_pairs : 1));
+  int64_t* kept_rows = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n_pairs > 0 ? n_pairs : 1));
+  uint8_t* kept = (uint8_t*)malloc((size_t)(n_pairs > 0 ? n_pairs : 1));
   float* wsub = (float*)malloc(sizeof(float) * (size_t)(n_pairs > 0 ? n_pairs : 1));
   double* yrows = y ? y : (double*)malloc(sizeof(double) * (size_t)(n_pairs > 0 ? n_pairs : 1) * (size_t)H);
+  int64_t n_kept = 0;
   for (int64_t i = 0; i < n_tok; ++i) {
     int64_t t = tokens ? tokens[i] : i;
     if (t < 0 || t >= M) { rc = ORC_EINVAL; break; }
     for (int j = 0; j < k; ++j) {
       rows[i * k + j] = flat_to_sorted[t * k + j];
+      kept[i * k + j] = rows[i * k + j] >= 0;
       wsub[i * k + j] = topk_w[t * k + j];
+      if (kept[i * k + j]) kept_rows[n_kept++] = rows[i * k + j];
     }
   }
+  /* the FFN runs for the kept pairs only; a dropped pair's rows hold zeros */
+  double* hk = (double*)malloc(sizeof(double) * (size_t)(n_kept > 0 ? n_kept : 1) * (size_t)F);
+  double* yk = (double*)malloc(sizeof(double) * (size_t)(n_kept > 0 ? n_kept : 1) * (size_t)H);
   if (!rc)
-    rc = orc_ffn_rows(H, F, E, S, k, dtype, x, w_gate, w_up, w_down, sorted_to_flat, offsets, n_pairs, rows, hact,
-                      yrows);
-  if (!rc) rc = orc_combine_tokens(H, k, n_tok, wsub, yrows, out);
+    rc = orc_ffn_rows(H, F, EL, S, k, dtype, x, w_gate, w_up, w_down, sorted_to_flat, offsets, n_kept, kept_rows,
+                      hk, yk);
+  if (!rc) {
+    int64_t q = 0;
+    for (int64_t p = 0; p < n_pairs; ++p) {
+      if (kept[p]) {
+        memcpy(yrows + p * H, yk + q * H, sizeof(double) * (size_t)H);
+        if (hact) memcpy(hact + p * F, hk + q * F, sizeof(double) * (size_t)F);
+        ++q;
+      } else {
+        memset(yrows + p * H, 0, sizeof(double) * (size_t)H);
+        if (hact) memset(hact + p * F, 0, sizeof(double) * (size_t)F);
+      }
+    }
+    rc = orc_combine_tokens(H, k, n_tok, wsub, yrows, kept, out);
+  }
   free(rows);
+  free(kept_rows);
+  free(kept);
   free(wsub);
+  free(hk);
+  free(yk);
   if (!y) free(yrows);
   return rc;
 }

@@ -31,11 +31,22 @@ MUTANTS = {
                         "g += xrow[h] * load_elem(w_gate, dtype, eHF + (int64_t)h * F + f);"),
     "combine_slot0_weight": ("acc += (double)topk_w_sub[i * k + j] * y_rows[(i * k + j) * H + n];",
                              "acc += (double)topk_w_sub[i * k] * y_rows[(i * k + j) * H + n];"),
-    "combine_drops_last_slot": ("for (int j = 0; j < k; ++j) acc += (double)topk_w_sub",
-                                "for (int j = 0; j + 1 < k; ++j) acc += (double)topk_w_sub"),
-    "unstable_permutation": ("for (int64_t f = 0; f < R; ++f)\n      if (seg_of(topk_idx, src_block, E, k, f) == g) sorted_to_flat[r++] = (int32_t)f;",
-                             "for (int64_t f = R - 1; f >= 0; --f)\n      if (seg_of(topk_idx, src_block, E, k, f) == g) sorted_to_flat[r++] = (int32_t)f;"),
-    "segment_key_unscaled": ("return s * E + topk_idx[f];", "return s + topk_idx[f];"),
+    "combine_drops_last_slot": ("for (int j = 0; j < k; ++j)\n        if (!kept",
+                                "for (int j = 0; j + 1 < k; ++j)\n        if (!kept"),
+    "unstable_permutation": ("for (int64_t f = 0; f < R; ++f)\n      if (seg_of(topk_idx, src_block, base, EL, k, f) == g)",
+                             "for (int64_t f = R - 1; f >= 0; --f)\n      if (seg_of(topk_idx, src_block, base, EL, k, f) == g)"),
+    "segment_key_unscaled": ("return s * EL + e;", "return s + e;"),
+    "local_filter_ignores_base": ("int64_t e = (int64_t)topk_idx[f] - base;", "int64_t e = (int64_t)topk_idx[f];"),
+    "local_filter_one_past": ("if (e < 0 || e >= EL) return -1;", "if (e < 0 || e > EL) return -1;"),
+    "local_tail_not_cleared": ("for (; r < R; ++r) sorted_to_flat[r] = -1;", ""),
+    "local_dropped_not_marked": ("for (int64_t f = 0; f < R; ++f) flat_to_sorted[f] = -1;",
+                                 "for (int64_t f = 0; f < R; ++f) flat_to_sorted[f] = 0;"),
+    "epilogue_ignores_residual": ("double v = acc[i] + (residual ? load_elem(residual, res_dtype, i) : 0.0);",
+                                  "double v = acc[i];"),
+    "epilogue_not_rounded": ("out[i] = (out_dtype == ORC_BF16) ? orc_round_to_bf16(v) : v;", "out[i] = v;"),
+    "epilogue_rounds_acc_first": ("double v = acc[i] + (residual ? load_elem(residual, res_dtype, i) : 0.0);",
+                                  "double v = ((out_dtype == ORC_BF16) ? orc_round_to_bf16(acc[i]) : acc[i]) + "
+                                  "(residual ? load_elem(residual, res_dtype, i) : 0.0);"),
     "expert_from_block_index": ("int e = (int)(g % E);", "int e = (int)((g / E) % E);"),
     "ffn_reads_flat_row": ("int64_t t = sorted_to_flat[r] / k;\n    double* xrow", "int64_t t = r / k;\n    double* xrow"),
     "dispatch_wrong_token": ("int64_t t = sorted_to_flat[r] / k;\n    memcpy", "int64_t t = sorted_to_flat[r] % k;\n    memcpy"),
@@ -60,6 +71,13 @@ def _checks():
         ("dense_bf16", lambda: pins.test_layer_matches_dense_brute_force("bf16", 6, 3)),
         ("dense_src_blocks", pins.test_layer_with_source_blocks_matches_dense),
         ("single_ffn", pins.test_top1_single_expert_is_one_dense_swiglu_ffn),
+        ("local_segments", lambda: pins.test_local_segments_brute_force(60, 16, 4, 1, 4, 4)),
+        ("local_segments_S4", lambda: pins.test_local_segments_brute_force(96, 32, 8, 4, 0, 8)),
+        ("local_last_expert", lambda: pins.test_local_segments_brute_force(33, 16, 2, 1, 15, 1)),
+        ("local_dense", lambda: pins.test_local_layer_matches_dense_partial("bf16", 16, 4, 12, 4)),
+        ("local_partition", pins.test_local_partition_sums_to_full_layer),
+        ("epilogue_hand", pins.test_epilogue_hand_values),
+        ("epilogue_torch", pins.test_epilogue_bf16_matches_torch_rounding_of_f32_sums),
     ]
 
 

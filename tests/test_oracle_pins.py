@@ -38,28 +38,30 @@ def widen(a):
     return moe_synth.bf16_bits_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else a.astype(np.float64)
 
 
-def dense_layer(x, logits, wg, wu, wd, k, bf16):
+def dense_layer(x, logits, wg, wu, wd, k, bf16, base=0):
     """Every expert on every token, then the top-k mask and weights.
 
     Independent of the oracle's routing / permutation / combine: experts are
     chosen by argsort, weights by the full softmax renormalised over the
-    selected experts, and the FFN runs as dense numpy matmuls."""
+    selected experts, and the FFN runs as dense numpy matmuls.  The weights
+    may hold experts base .. base + len(wg) - 1 of the logits' experts only:
+    then only those experts' terms are summed."""
     X = widen(x)
     L = logits.astype(np.float64)
     M, E = L.shape
-    Wg, Wu, Wd = widen(wg), widen(wu), widen(wd)  # [E,F,H], [E,F,H], [E,H,F]
+    Wg, Wu, Wd = widen(wg), widen(wu), widen(wd)  # [EL,F,H], [EL,F,H], [EL,H,F]
     out = np.zeros((M, X.shape[1]))
     # selection: stable argsort of -logit gives ties to the lower index
     order = np.argsort(-L, axis=1, kind="stable")[:, :k]
     p = np.exp(L - L.max(axis=1, keepdims=True))
     p = p / p.sum(axis=1, keepdims=True)
-    for e in range(E):
-        G = X @ Wg[e].T
-        U = X @ Wu[e].T
+    for e in range(base, base + Wg.shape[0]):
+        G = X @ Wg[e - base].T
+        U = X @ Wu[e - base].T
         Hh = G / (1.0 + np.exp(-G)) * U
         if bf16:
             Hh = np.vectorize(oracle.round_to_bf16)(Hh)
-        Y = Hh @ Wd[e].T
+        Y = Hh @ Wd[e - base].T
         sel = (order == e)
         mask = sel.any(axis=1)
         w = np.where(mask, p[:, e] / np.take_along_axis(p, order, axis=1).sum(axis=1), 0.0)
@@ -270,3 +272,118 @@ def test_unskewed_configs_are_near_uniform():
     counts, _ = oracle.counts_offsets(idx, cfg.E)
     frac = counts / float(cfg.R)
     assert frac.std() < 0.25 / cfg.E
+
+
+# ------------------------------------------------- local experts (EP share) --
+# A call that holds experts [base, base + EL) of E keeps only the pairs routed
+# to them (COMET review §4.1.2 dispatch by source and expert; the PTO MoE
+# article's 16 local experts per card), and its combine is that holder's
+# share of each token's sum.
+
+@pytest.mark.parametrize("M,E,k,S,base,EL", [(60, 16, 4, 1, 4, 4), (96, 32, 8, 4, 0, 8), (50, 8, 2, 2, 6, 2),
+                                             (40, 8, 2, 1, 0, 8), (33, 16, 2, 1, 15, 1), (0, 8, 2, 1, 2, 3)])
+def test_local_segments_brute_force(M, E, k, S, base, EL):
+    rng = np.random.default_rng(M * 13 + E + base)
+    logits = rng.standard_normal((M, E)).astype(np.float32)
+    idx, _ = oracle.route(logits, k)
+    src = None if S == 1 else (np.arange(M) * S // max(M, 1)).astype(np.int32)
+    counts, offsets = oracle.counts_offsets(idx, E, S, src, base, EL)
+    s2f, f2s = oracle.permutation(idx, E, S, src, base, EL)
+    R = M * k
+    flat_e = idx.reshape(-1)
+    kept = [f for f in range(R) if base <= flat_e[f] < base + EL]
+    seg = {f: (0 if src is None else int(src[f // k])) * EL + int(flat_e[f]) - base for f in kept}
+    want = sorted(kept, key=lambda f: (seg[f], f))
+    n = len(want)
+    assert counts.shape == (S * EL,) and offsets.shape == (S * EL + 1,)
+    assert list(s2f[:n]) == want and np.all(s2f[n:] == -1)
+    assert offsets[0] == 0 and offsets[-1] == n and np.all(np.diff(offsets) == counts)
+    for f in range(R):
+        assert f2s[f] == (want.index(f) if f in seg else -1)
+
+
+def test_local_full_range_is_the_plain_layer():
+    cfg, d = small_inputs(40, 64, 64, 8, 2, "bf16", 51, S=2)
+    a = oracle.moe_layer(d["x"], d["logits"], d["w_gate"], d["w_up"], d["w_down"], 2, S=2, src_block=d["src_block"])
+    b = oracle.moe_layer(d["x"], d["logits"], d["w_gate"], d["w_up"], d["w_down"], 2, S=2, src_block=d["src_block"],
+                         expert_base=0, local_experts=8)
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("dtype,E,k,base,EL", [("f32", 8, 2, 2, 3), ("bf16", 16, 4, 12, 4), ("bf16", 8, 8, 0, 1)])
+def test_local_layer_matches_dense_partial(dtype, E, k, base, EL):
+    cfg, d = small_inputs(48, 64, 96, E, k, dtype, 61 + E + base)
+    sl = slice(base, base + EL)
+    r = oracle.moe_layer(d["x"], d["logits"], d["w_gate"][sl], d["w_up"][sl], d["w_down"][sl], k,
+                         expert_base=base, local_experts=EL)
+    dense, order = dense_layer(d["x"], d["logits"], d["w_gate"][sl], d["w_up"][sl], d["w_down"][sl], k,
+                               dtype == "bf16", base=base)
+    assert np.array_equal(r["topk_idx"], order)
+    np.testing.assert_allclose(r["out"], dense, rtol=1e-9, atol=1e-12)
+
+
+def test_local_partition_sums_to_full_layer():
+    """Four holders of 4 experts each: their counts are the full counts,
+    source block by source block, and their partial outputs add up to the
+    full layer's output."""
+    cfg, d = small_inputs(64, 64, 64, 16, 4, "bf16", 71, S=2)
+    full = oracle.moe_layer(d["x"], d["logits"], d["w_gate"], d["w_up"], d["w_down"], 4, S=2,
+                            src_block=d["src_block"])
+    total = np.zeros_like(full["out"])
+    for b in range(0, 16, 4):
+        sl = slice(b, b + 4)
+        part = oracle.moe_layer(d["x"], d["logits"], d["w_gate"][sl], d["w_up"][sl], d["w_down"][sl], 4, S=2,
+                                src_block=d["src_block"], expert_base=b, local_experts=4)
+        for s in range(2):
+            assert np.array_equal(part["counts"][s * 4:(s + 1) * 4], full["counts"][s * 16 + b:s * 16 + b + 4])
+        total += part["out"]
+    np.testing.assert_allclose(total, full["out"], rtol=1e-12, atol=1e-13)
+
+
+# -------------------------------------------------------------- epilogue --
+# cast(acc + residual) (grouped-GEMM article, fused GemmAdd epilogue).
+
+def test_epilogue_hand_values():
+    b = lambda v: moe_synth.to_bf16_bits(np.float32([v]))  # noqa: E731  exact bf16 residuals
+    # 1 + 2^-8 lies halfway between the bf16 values 1 and 1 + 2^-7: to even (1)
+    assert oracle.epilogue(np.array([1.0]), b(2.0 ** -8), "bf16")[0] == 1.0
+    # a little above halfway rounds up
+    assert oracle.epilogue(np.array([1.0 + 2.0 ** -12]), b(2.0 ** -8), "bf16")[0] == 1.0 + 2.0 ** -7
+    # 257 lies halfway between 256 and 258: to even (256); 259 -> 260
+    assert oracle.epilogue(np.array([256.0]), b(1.0), "bf16")[0] == 256.0
+    assert oracle.epilogue(np.array([256.0]), b(3.0), "bf16")[0] == 260.0
+    # negative, f32 residual, f32 output: the plain sum
+    assert oracle.epilogue(np.array([-2.5]), np.float32([0.25]), "f32")[0] == -2.25
+    assert oracle.epilogue(np.array([0.1]), None, "f32")[0] == 0.1
+    # 1 + 3 * 2^-9 is above halfway between 1 and 1 + 2^-7 -> up; -(that) -> down
+    assert oracle.epilogue(np.array([1.0, -1.0]), np.float32([3 * 2.0 ** -9, -3 * 2.0 ** -9]), "bf16").tolist() == \
+        [1.0 + 2.0 ** -7, -1.0 - 2.0 ** -7]
+
+
+def test_epilogue_bf16_matches_torch_rounding_of_f32_sums():
+    rng = np.random.default_rng(81)
+    # both operands on the grid of 2^-12 with magnitude below 8: every sum
+    # is a multiple of 2^-12 below 16, exact in f32, so torch rounds it once
+    grid = lambda v: np.clip(np.round(v * 4096.0), -32000, 32000) / 4096.0  # noqa: E731
+    acc = grid(rng.standard_normal(5000) * 2.0)
+    res = moe_synth.to_bf16_bits(grid(rng.standard_normal(5000) * 2.0).astype(np.float32))
+    res_v = moe_synth.bf16_bits_to_f32(res).astype(np.float64)
+    got = oracle.epilogue(acc, res, "bf16")
+    exact = acc + res_v
+    assert np.array_equal(exact.astype(np.float32).astype(np.float64), exact)
+    want = torch.from_numpy(exact.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(got, want)
+
+
+def test_layer_epilogue_is_applied_to_the_combined_output():
+    cfg, d = small_inputs(24, 64, 64, 4, 2, "bf16", 91)
+    res = moe_synth.to_bf16_bits(np.random.default_rng(92).standard_normal((24, 64)).astype(np.float32))
+    toks = np.array([3, 0, 17, 23])
+    r = oracle.moe_layer(d["x"], d["logits"], d["w_gate"], d["w_up"], d["w_down"], 2, tokens=toks, residual=res,
+                         out_dtype="bf16")
+    plain = oracle.moe_layer(d["x"], d["logits"], d["w_gate"], d["w_up"], d["w_down"], 2, tokens=toks)
+    assert np.array_equal(r["acc"], plain["out"])
+    want = torch.from_numpy((plain["out"] + widen(res)[toks]).astype(np.float32)).to(torch.bfloat16).double()
+    # the f32 rounding of the sum is within half an f32 ulp: the bf16 results agree except at exact ties
+    assert np.mean(r["out"] == want.numpy()) > 0.999

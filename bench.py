@@ -100,13 +100,14 @@ def cpu_baseline(cfg, d, target_s):
     """The oracle as it stands, on a seeded token sample sized for ~target_s."""
     import moe_synth
     import oracle
-    flop_tok = 6.0 * cfg.k * cfg.H * cfg.F
+    flop_pair = 6.0 * cfg.H * cfg.F
+    held = dict(expert_base=cfg.base, local_experts=cfg.local)
 
     def timed(n_tok, tag):
         toks = moe_synth.token_sample(cfg, n_tok, seed_tag=tag)
         t0 = time.perf_counter()
         oracle.moe_layer(d["x"], d["logits"], d["w_gate"], d["w_up"], d["w_down"], cfg.k, S=cfg.S,
-                         src_block=d["src_block"], tokens=toks)
+                         src_block=d["src_block"], tokens=toks, **held)
         return len(toks), time.perf_counter() - t0
 
     # two probe sizes separate the fixed cost (full routing of every token)
@@ -118,12 +119,14 @@ def cpu_baseline(cfg, d, target_s):
     n = int(max(cfg.S, min(cfg.M, round((target_s - fixed) / per_tok))))
     toks = moe_synth.token_sample(cfg, n, seed_tag=12)
     t0 = time.perf_counter()
-    oracle.moe_layer(d["x"], d["logits"], d["w_gate"], d["w_up"], d["w_down"], cfg.k, S=cfg.S,
-                     src_block=d["src_block"], tokens=toks)
+    r = oracle.moe_layer(d["x"], d["logits"], d["w_gate"], d["w_up"], d["w_down"], cfg.k, S=cfg.S,
+                         src_block=d["src_block"], tokens=toks, **held)
     dt = time.perf_counter() - t0
-    flops = flop_tok * len(toks)
+    # FFN work only for the pairs whose expert is held
+    pairs = int((r["flat_to_sorted"].reshape(cfg.M, cfg.k)[toks] >= 0).sum())
+    flops = flop_pair * pairs
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{len(toks)} of {cfg.M} tokens (all {cfg.k} routed rows each, seeded), full routing; "
+            "sample": f"{len(toks)} of {cfg.M} tokens ({pairs} held routed rows, seeded), full routing; "
                       f"{dt:.1f} s fp64 on the host; per-token work is exactly linear, so the full layer "
                       f"would take {dt * cfg.M / len(toks):.0f} s"}
 
@@ -157,8 +160,8 @@ def main():
     d = moe_synth.make_inputs(cfg)
     g = upload(d)
     dev = torch.device("cuda:0")
-    p = moe.problem(cfg.M, cfg.H, cfg.F, cfg.E, cfg.k, cfg.S, cfg.dtype)
-    M, k, H, F, G, R = cfg.M, cfg.k, cfg.H, cfg.F, cfg.S * cfg.E, cfg.R
+    p = moe.problem(cfg.M, cfg.H, cfg.F, cfg.E, cfg.k, cfg.S, cfg.dtype, cfg.base, cfg.local)
+    M, k, H, F, G, R = cfg.M, cfg.k, cfg.H, cfg.F, cfg.S * cfg.EL, cfg.R
     act = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     idx = torch.empty((M, k), dtype=torch.int32, device=dev)
     w = torch.empty((M, k), dtype=torch.float32, device=dev)
@@ -219,16 +222,34 @@ def main():
     #     calls: per-step times and the dominant kernel's live duration
     ms_chain, per = time_steps(step_chain, 6, args.warmup, args.steps)
 
-    flops = 6.0 * R * H * F
+    # (3) the combine with the output epilogue: a bf16 residual added and the
+    #     result cast to bf16 (the option a model layer would use)
+    res_in = torch.randn((M, H), generator=torch.Generator().manual_seed(3)).to(act).to(dev)
+    out_bf16 = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    epi = moe.epilogue(res_in, "bf16")
+
+    def step_epilogue(ev):
+        if ev: ev[0].record(stream)
+        moe.moe_combine_ex(p, y, w, f2s, epi, out_bf16, stream)
+        if ev: ev[1].record(stream)
+
+    _, per_epi = time_steps(step_epilogue, 2, args.warmup, args.steps)
+
+    # pairs routed to held experts (all of them unless only some are held)
+    Rk = int(offsets[-1].item())
+    Tk = int((f2s.view(M, k) >= 0).any(dim=1).sum().item())
+    flops = 6.0 * Rk * H * F
     movers = moe.moe_layer_default_movers(p) if args.n_mover < 0 else args.n_mover
     res = {"metric": "MoE layer us + grouped-GEMM TFLOP/s (% MFMA peak), Mixtral shape M=8192",
            "value": flops / (ms_step * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
            "data": "synthetic (seeded N(0,1) tokens and logits, N(0,0.02^2) weights, random-init)",
-           "config": {"workload": f"{cfg.name}: MoE layer M={M} H={H} F={F} E={cfg.E} topk={k} S={cfg.S}",
+           "config": {"workload": f"{cfg.name}: MoE layer M={M} H={H} F={F} E={cfg.E} topk={k} S={cfg.S}"
+                      + (f" experts held {cfg.base}..{cfg.base + cfg.EL - 1}" if cfg.local else ""),
                       "tokens": M, "hidden": H, "ffn": F, "experts": cfg.E, "topk": k, "src_blocks": cfg.S,
-                      "layer_call": "fused" if (args.mode == "layer" and movers > 0 and cfg.dtype == "bf16")
+                      "experts_held": cfg.EL, "routed_rows_held": Rk,
+                      "layer_call": "fused" if (args.mode == "layer" and movers >= 0 and cfg.dtype == "bf16")
                       else "chain", "n_mover": movers},
            "layer_us": ms_step * 1e3, "chain_us": ms_chain * 1e3}
     mean = per.mean(axis=0)
@@ -239,8 +260,12 @@ def main():
     res["grouped_gemm_tflops"] = flops / t_gemm / 1e12
     res["grouped_gemm_pct_peak"] = 100.0 * res["grouped_gemm_tflops"] / peak
     eb = 2 if cfg.dtype == "bf16" else 4
-    disp_bytes = M * H * eb * (1 + k) + R * 4
-    comb_bytes = R * H * 4 + M * H * 4 + M * k * 8
+    # token rows read (those with a held pair), rows written, the index list
+    disp_bytes = Tk * H * eb + Rk * H * eb + R * 4
+    comb_bytes = Rk * H * 4 + M * H * 4 + M * k * 8
+    epi_bytes = Rk * H * 4 + M * H * eb + M * H * 2 + M * k * 8
+    res["combine_epilogue_us"] = float(per_epi.mean())
+    res["combine_epilogue_gbs"] = epi_bytes / (per_epi.mean() * 1e-6) / 1e9
     res["dispatch_gbs"] = disp_bytes / (mean[1] * 1e-6) / 1e9
     res["combine_gbs"] = comb_bytes / (mean[4] * 1e-6) / 1e9
     res["dispatch_pct_hbm"] = 100.0 * res["dispatch_gbs"] / PEAK_HBM_GBS
@@ -249,7 +274,7 @@ def main():
     # movement (dispatch + combine) that the fused step hides behind the GEMMs
     move = mean[1] + mean[4]
     res["movement_hidden_pct"] = 100.0 * (1.0 - (ms_step * 1e3 - mean[0] - mean[2] - mean[3]) / move)
-    l0_flops = 4.0 * R * H * F
+    l0_flops = 4.0 * Rk * H * F
     ach = l0_flops / (mean[2] * 1e-6) / 1e12
     res["roofline"] = {"kernel": "grouped_gemm_bf16_kernel<0> (Layer0 gate/up + SwiGLU), chain timing",
                        "bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak,

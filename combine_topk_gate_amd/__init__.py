@@ -8,7 +8,8 @@ the stream given) straight through.  There is no fallback: if the library is
 missing, loading it raises.
 
 The entry points keep the C names: ``moe_route``, ``moe_dispatch``,
-``moe_grouped_gemm``, ``moe_combine``, ``moe_layer`` (plus
+``moe_grouped_gemm``, ``moe_combine``, ``moe_combine_ex``, ``moe_layer``,
+``moe_layer_ex`` (plus
 ``moe_workspace_bytes``, ``moe_layer_default_movers``,
 ``moe_debug_device_status``, ``moe_status_string``, ``moe_abi_version``).
 """
@@ -34,8 +35,9 @@ MOE_OP_DISPATCH = 0
 MOE_OP_GROUPED_GEMM = 1
 MOE_OP_LAYER = 2
 
-EXPORTED = ("moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_grouped_gemm", "moe_combine", "moe_layer",
-            "moe_layer_default_movers", "moe_debug_device_status", "moe_status_string", "moe_abi_version")
+EXPORTED = ("moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_grouped_gemm", "moe_combine", "moe_combine_ex",
+            "moe_layer", "moe_layer_ex", "moe_layer_default_movers", "moe_debug_device_status", "moe_status_string",
+            "moe_abi_version")
 
 
 class MoeError(RuntimeError):
@@ -47,7 +49,11 @@ class MoeError(RuntimeError):
 class Problem(ctypes.Structure):
     _fields_ = [("num_tokens", ctypes.c_int64), ("hidden", ctypes.c_int32), ("ffn", ctypes.c_int32),
                 ("num_experts", ctypes.c_int32), ("topk", ctypes.c_int32), ("num_src_blocks", ctypes.c_int32),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("expert_base", ctypes.c_int32), ("local_experts", ctypes.c_int32)]
+
+
+class Epilogue(ctypes.Structure):
+    _fields_ = [("residual", ctypes.c_void_p), ("out_dtype", ctypes.c_int32)]
 
 
 class LayerAux(ctypes.Structure):
@@ -80,7 +86,10 @@ def load_library(path: str = LIB_PATH):
         "moe_dispatch": ([PP, P, P, P, P, P, P, P, P, P, SZ, P], I32),
         "moe_grouped_gemm": ([PP, I32, P, P, P, P, P, P, SZ, P], I32),
         "moe_combine": ([PP, P, P, P, P, P], I32),
+        "moe_combine_ex": ([PP, P, P, P, ctypes.POINTER(Epilogue), P, P], I32),
         "moe_layer": ([PP, P, P, P, P, P, P, P, ctypes.POINTER(LayerAux), ctypes.POINTER(LayerOpts), P, SZ, P], I32),
+        "moe_layer_ex": ([PP, P, P, P, P, P, P, ctypes.POINTER(Epilogue), P, ctypes.POINTER(LayerAux),
+                          ctypes.POINTER(LayerOpts), P, SZ, P], I32),
         "moe_layer_default_movers": ([PP], I32),
         "moe_debug_device_status": ([PP, P, SZ, P], I32),
         "moe_status_string": ([I32], ctypes.c_char_p),
@@ -101,10 +110,17 @@ def status_name(status: int) -> str:
         return str(status)
 
 
-def problem(M, H, F, E, k, S=1, dtype="bf16") -> Problem:
-    dt = {"bf16": MOE_DTYPE_BF16, "f32": MOE_DTYPE_F32, MOE_DTYPE_BF16: MOE_DTYPE_BF16,
-          MOE_DTYPE_F32: MOE_DTYPE_F32}[dtype]
-    return Problem(int(M), int(H), int(F), int(E), int(k), int(S), dt)
+_DTYPES = {"bf16": MOE_DTYPE_BF16, "f32": MOE_DTYPE_F32, MOE_DTYPE_BF16: MOE_DTYPE_BF16, MOE_DTYPE_F32: MOE_DTYPE_F32}
+
+
+def problem(M, H, F, E, k, S=1, dtype="bf16", expert_base=0, local_experts=0) -> Problem:
+    return Problem(int(M), int(H), int(F), int(E), int(k), int(S), _DTYPES[dtype], int(expert_base),
+                   int(local_experts))
+
+
+def epilogue(residual=None, out_dtype="f32") -> Epilogue:
+    """The combine's output epilogue: out = cast(acc + residual)."""
+    return Epilogue(None if residual is None else residual.data_ptr(), _DTYPES[out_dtype])
 
 
 def _ptr(t):
@@ -167,6 +183,12 @@ def moe_combine(p, y, topk_w, flat_to_sorted, out, stream=None):
                                       _stream(stream)), "moe_combine")
 
 
+def moe_combine_ex(p, y, topk_w, flat_to_sorted, epi, out, stream=None):
+    _check(load_library().moe_combine_ex(ctypes.byref(p), _ptr(y), _ptr(topk_w), _ptr(flat_to_sorted),
+                                         ctypes.byref(epi) if epi is not None else None, _ptr(out),
+                                         _stream(stream)), "moe_combine_ex")
+
+
 def moe_layer(p, x, logits, src_block, w_gate, w_up, w_down, out, ws, aux: dict | None = None,
               n_mover: int = -1, grid: int = 0, fused: int = 1, spin_limit: int = 0, stream=None):
     a = None
@@ -176,6 +198,18 @@ def moe_layer(p, x, logits, src_block, w_gate, w_up, w_down, out, ws, aux: dict 
     _check(load_library().moe_layer(ctypes.byref(p), _ptr(x), _ptr(logits), _ptr(src_block), _ptr(w_gate),
                                     _ptr(w_up), _ptr(w_down), _ptr(out), ctypes.byref(a) if a else None,
                                     ctypes.byref(o), _ptr(ws), _nbytes(ws), _stream(stream)), "moe_layer")
+
+
+def moe_layer_ex(p, x, logits, src_block, w_gate, w_up, w_down, epi, out, ws, aux: dict | None = None,
+                 n_mover: int = -1, grid: int = 0, fused: int = 1, spin_limit: int = 0, stream=None):
+    a = None
+    if aux:
+        a = LayerAux(**{k: (v.data_ptr() if v is not None else None) for k, v in aux.items()})
+    o = LayerOpts(int(n_mover), int(grid), int(fused), int(spin_limit))
+    _check(load_library().moe_layer_ex(ctypes.byref(p), _ptr(x), _ptr(logits), _ptr(src_block), _ptr(w_gate),
+                                       _ptr(w_up), _ptr(w_down), ctypes.byref(epi) if epi is not None else None,
+                                       _ptr(out), ctypes.byref(a) if a else None, ctypes.byref(o), _ptr(ws),
+                                       _nbytes(ws), _stream(stream)), "moe_layer_ex")
 
 
 def moe_debug_device_status(p, ws, stream=None) -> int:

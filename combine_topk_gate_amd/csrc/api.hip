@@ -19,6 +19,12 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 size_t elem_bytes(const moe_problem_t* p) { return p->dtype == MOE_DTYPE_BF16 ? 2 : 4; }
 
+// Experts held by the call (weights it is given): EL, or all E.
+int held(const moe_problem_t* p) { return p->local_experts > 0 ? p->local_experts : p->num_experts; }
+int held_base(const moe_problem_t* p) { return p->local_experts > 0 ? p->expert_base : 0; }
+// Segments: S * EL.
+int segments(const moe_problem_t* p) { return p->num_src_blocks * held(p); }
+
 moe_status_t check_problem(const moe_problem_t* p) {
   if (!p) return MOE_ERR_INVALID_ARGUMENT;
   const int64_t M = p->num_tokens;
@@ -27,13 +33,38 @@ moe_status_t check_problem(const moe_problem_t* p) {
   if (p->ffn < 64 || p->ffn > 65536 || p->ffn % 64) return MOE_ERR_INVALID_ARGUMENT;
   if (p->num_experts < 1 || p->num_experts > 512) return MOE_ERR_INVALID_ARGUMENT;
   if (p->topk < 1 || p->topk > 16 || p->topk > p->num_experts) return MOE_ERR_INVALID_ARGUMENT;
-  if (p->num_src_blocks < 1 || (int64_t)p->num_src_blocks * p->num_experts > 1024) return MOE_ERR_INVALID_ARGUMENT;
+  if (p->local_experts < 0 || p->expert_base < 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (p->local_experts == 0 && p->expert_base != 0) return MOE_ERR_INVALID_ARGUMENT;
+  if ((int64_t)p->expert_base + p->local_experts > p->num_experts) return MOE_ERR_INVALID_ARGUMENT;
+  // dropped pairs take one more segment in the bookkeeping
+  const int64_t ranked = (int64_t)p->num_src_blocks * held(p) + (held(p) < p->num_experts ? 1 : 0);
+  if (p->num_src_blocks < 1 || ranked > 1024) return MOE_ERR_INVALID_ARGUMENT;
   if (p->dtype != MOE_DTYPE_F32 && p->dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARGUMENT;
   const int64_t R = M * p->topk;
   if (R >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
   const int64_t wide = p->hidden > p->ffn ? p->hidden : p->ffn;
   if (R * wide >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
-  if ((int64_t)p->num_experts * p->hidden * p->ffn >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)held(p) * p->hidden * p->ffn >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+PermutePlan plan_of(const moe_problem_t* p) {
+  return permute_plan(p->num_tokens, p->topk, p->num_src_blocks, p->num_experts, held_base(p), p->local_experts);
+}
+
+// Epilogue of the combine from the caller's description (null: plain f32).
+moe_status_t epilogue_of(const moe_problem_t* p, const moe_epilogue_t* epi, void* out, OutEpilogue* ep) {
+  ep->out = out;
+  ep->residual = nullptr;
+  ep->res_bf16 = p->dtype == MOE_DTYPE_BF16;
+  ep->out_bf16 = 0;
+  if (epi) {
+    if (epi->out_dtype != MOE_DTYPE_F32 && epi->out_dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARGUMENT;
+    ep->out_bf16 = epi->out_dtype == MOE_DTYPE_BF16;
+    ep->residual = epi->residual;
+    if (epi->residual && ((uintptr_t)epi->residual % 16)) return MOE_ERR_INVALID_ARGUMENT;
+  }
+  if ((uintptr_t)out % 16) return MOE_ERR_INVALID_ARGUMENT;
   return MOE_OK;
 }
 
@@ -46,9 +77,9 @@ struct LayerWs {
 
 LayerWs layer_ws(const moe_problem_t* p) {
   const int64_t M = p->num_tokens, R = M * p->topk;
-  const int G = p->num_src_blocks * p->num_experts;
+  const int G = segments(p);
   const size_t eb = elem_bytes(p);
-  const PermutePlan pl = permute_plan(M, p->topk, G);
+  const PermutePlan pl = plan_of(p);
   LayerWs w;
   size_t o = 0;
   w.status = o; o += align_up(kAlign);
@@ -62,7 +93,7 @@ LayerWs layer_ws(const moe_problem_t* p) {
   w.x_perm = o; o += align_up((size_t)R * p->hidden * eb);
   w.hact = o; o += align_up((size_t)R * p->ffn * eb);
   w.y = o; o += align_up((size_t)R * p->hidden * 4);
-  w.fused = o; o += align_up(fused_ws_bytes(p->num_tokens, p->hidden, p->ffn, p->num_experts, p->topk,
+  w.fused = o; o += align_up(fused_ws_bytes(p->num_tokens, p->hidden, p->ffn, held(p), p->topk,
                                              p->num_src_blocks));
   w.gemm = o; o += align_up(p->dtype == MOE_DTYPE_BF16 ? gemm_split_ws_bytes() : 0);
   w.total = o;
@@ -78,7 +109,7 @@ T* at(void* ws, size_t off) {
 
 extern "C" {
 
-int32_t moe_abi_version(void) { return (1 << 16) | 0; }
+int32_t moe_abi_version(void) { return (2 << 16) | 0; }
 
 const char* moe_status_string(moe_status_t s) {
   switch (s) {
@@ -94,9 +125,8 @@ const char* moe_status_string(moe_status_t s) {
 
 size_t moe_workspace_bytes(const moe_problem_t* p, int32_t op) {
   if (check_problem(p) != MOE_OK) return 0;
-  const int G = p->num_src_blocks * p->num_experts;
   switch (op) {
-    case MOE_OP_DISPATCH: return permute_ws_bytes(permute_plan(p->num_tokens, p->topk, G));
+    case MOE_OP_DISPATCH: return permute_ws_bytes(plan_of(p));
     case MOE_OP_GROUPED_GEMM: return p->dtype == MOE_DTYPE_BF16 ? gemm_split_ws_bytes() : 0;
     case MOE_OP_LAYER: return layer_ws(p).total;
   }
@@ -125,12 +155,11 @@ moe_status_t moe_dispatch(const moe_problem_t* p, const void* x, const int32_t* 
     if (!x || !topk_idx || !sorted_to_flat || !flat_to_sorted || !x_perm) return MOE_ERR_INVALID_ARGUMENT;
     if (!aligned(x, 16) || !aligned(x_perm, 16)) return MOE_ERR_INVALID_ARGUMENT;
   }
-  const int G = p->num_src_blocks * p->num_experts;
-  const PermutePlan pl = permute_plan(M, p->topk, G);
+  const PermutePlan pl = plan_of(p);
   if (ws_bytes < permute_ws_bytes(pl) || !ws) return MOE_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_permute(pl, topk_idx, p->num_src_blocks > 1 ? src_block : nullptr, p->num_experts, p->topk,
-                                counts, offsets, sorted_to_flat, flat_to_sorted, (int32_t*)ws, s);
+  hipError_t e = launch_permute(pl, topk_idx, p->num_src_blocks > 1 ? src_block : nullptr, p->topk, counts, offsets,
+                                sorted_to_flat, flat_to_sorted, (int32_t*)ws, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = launch_dispatch_copy(x, M, (int64_t)p->hidden * elem_bytes(p), p->topk, flat_to_sorted, x_perm, s);
   return hip_status(e);
@@ -156,8 +185,8 @@ moe_status_t moe_grouped_gemm(const moe_problem_t* p, int32_t layer, const void*
   gp.R = R;
   gp.K = layer == 0 ? p->hidden : p->ffn;
   gp.N = layer == 0 ? p->ffn : p->hidden;
-  gp.E = p->num_experts;
-  gp.G = p->num_src_blocks * p->num_experts;
+  gp.E = held(p);
+  gp.G = segments(p);
   // a workspace smaller than moe_workspace_bytes(p, MOE_OP_GROUPED_GEMM)
   // (or none) only disables the split of the last round
   if (ws && !aligned(ws, 16)) return MOE_ERR_INVALID_ARGUMENT;
@@ -167,15 +196,23 @@ moe_status_t moe_grouped_gemm(const moe_problem_t* p, int32_t layer, const void*
   return hip_status(p->dtype == MOE_DTYPE_BF16 ? launch_grouped_gemm_bf16(gp, s) : launch_grouped_gemm_f32(gp, s));
 }
 
-moe_status_t moe_combine(const moe_problem_t* p, const float* y, const float* topk_w, const int32_t* flat_to_sorted,
-                         float* out, void* stream) {
+moe_status_t moe_combine_ex(const moe_problem_t* p, const float* y, const float* topk_w,
+                            const int32_t* flat_to_sorted, const moe_epilogue_t* epi, void* out, void* stream) {
   moe_status_t st = check_problem(p);
   if (st != MOE_OK) return st;
   if (p->num_tokens == 0) return MOE_OK;
   if (!y || !topk_w || !flat_to_sorted || !out) return MOE_ERR_INVALID_ARGUMENT;
-  if (!aligned(y, 16) || !aligned(out, 16) || !aligned(topk_w, 4)) return MOE_ERR_INVALID_ARGUMENT;
-  return hip_status(launch_combine(y, topk_w, flat_to_sorted, p->num_tokens, p->hidden, p->topk, out,
+  if (!aligned(y, 16) || !aligned(topk_w, 4)) return MOE_ERR_INVALID_ARGUMENT;
+  OutEpilogue ep;
+  st = epilogue_of(p, epi, out, &ep);
+  if (st != MOE_OK) return st;
+  return hip_status(launch_combine(y, topk_w, flat_to_sorted, p->num_tokens, p->hidden, p->topk, ep,
                                    (hipStream_t)stream));
+}
+
+moe_status_t moe_combine(const moe_problem_t* p, const float* y, const float* topk_w, const int32_t* flat_to_sorted,
+                         float* out, void* stream) {
+  return moe_combine_ex(p, y, topk_w, flat_to_sorted, nullptr, out, stream);
 }
 
 int32_t moe_layer_default_movers(const moe_problem_t* p) {
@@ -184,18 +221,21 @@ int32_t moe_layer_default_movers(const moe_problem_t* p) {
                               p->dtype, device_cu_count());
 }
 
-moe_status_t moe_layer(const moe_problem_t* p, const void* x, const float* logits, const int32_t* src_block,
-                       const void* w_gate, const void* w_up, const void* w_down, float* out,
-                       const moe_layer_aux_t* aux, const moe_layer_opts_t* opts, void* ws, size_t ws_bytes,
-                       void* stream) {
+moe_status_t moe_layer_ex(const moe_problem_t* p, const void* x, const float* logits, const int32_t* src_block,
+                          const void* w_gate, const void* w_up, const void* w_down, const moe_epilogue_t* epi,
+                          void* out, const moe_layer_aux_t* aux, const moe_layer_opts_t* opts, void* ws,
+                          size_t ws_bytes, void* stream) {
   moe_status_t st = check_problem(p);
   if (st != MOE_OK) return st;
   const int64_t M = p->num_tokens;
   if (!w_gate || !w_up || !w_down) return MOE_ERR_INVALID_ARGUMENT;
   if (M > 0 && (!x || !logits || !out)) return MOE_ERR_INVALID_ARGUMENT;
   if (p->num_src_blocks > 1 && !src_block && M > 0) return MOE_ERR_INVALID_ARGUMENT;
-  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(w_down, 16))
+  if (!aligned(x, 16) || !aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(w_down, 16))
     return MOE_ERR_INVALID_ARGUMENT;
+  OutEpilogue ep;
+  st = epilogue_of(p, epi, out, &ep);
+  if (st != MOE_OK) return st;
   const LayerWs L = layer_ws(p);
   if (!ws || ws_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
   if (!aligned(ws, kAlign)) return MOE_ERR_INVALID_ARGUMENT;
@@ -205,7 +245,7 @@ moe_status_t moe_layer(const moe_problem_t* p, const void* x, const float* logit
   if (a.x_perm && !aligned(a.x_perm, 16)) return MOE_ERR_INVALID_ARGUMENT;
   if (a.hact && !aligned(a.hact, 16)) return MOE_ERR_INVALID_ARGUMENT;
   if (a.y && !aligned(a.y, 16)) return MOE_ERR_INVALID_ARGUMENT;
-  const int G = p->num_src_blocks * p->num_experts;
+  const int G = segments(p);
   int32_t* idx = a.topk_idx ? a.topk_idx : at<int32_t>(ws, L.topk_idx);
   float* w = a.topk_w ? a.topk_w : at<float>(ws, L.topk_w);
   int32_t* counts = a.counts ? a.counts : at<int32_t>(ws, L.counts);
@@ -238,8 +278,8 @@ moe_status_t moe_layer(const moe_problem_t* p, const void* x, const float* logit
   }
   e = launch_route(logits, M, p->num_experts, p->topk, idx, w, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  const PermutePlan pl = permute_plan(M, p->topk, G);
-  e = launch_permute(pl, idx, src, p->num_experts, p->topk, counts, offsets, s2f, f2s, at<int32_t>(ws, L.perm), s);
+  const PermutePlan pl = plan_of(p);
+  e = launch_permute(pl, idx, src, p->topk, counts, offsets, s2f, f2s, at<int32_t>(ws, L.perm), s);
   if (e != hipSuccess) return MOE_ERR_HIP;
 
   const int cus = device_cu_count();
@@ -253,7 +293,7 @@ moe_status_t moe_layer(const moe_problem_t* p, const void* x, const float* logit
     fa.M = M;
     fa.H = p->hidden;
     fa.F = p->ffn;
-    fa.E = p->num_experts;
+    fa.E = held(p);
     fa.k = p->topk;
     fa.G = G;
     fa.x = x;
@@ -266,7 +306,7 @@ moe_status_t moe_layer(const moe_problem_t* p, const void* x, const float* logit
     fa.f2s = f2s;
     fa.hact = hact;
     fa.y = y;
-    fa.out = out;
+    fa.out = ep;
     fa.status = status;
     fa.flags = at<int32_t>(ws, L.fused);
     fa.mt_max = fused_mt_max(M, p->hidden, p->topk, G);
@@ -287,7 +327,7 @@ moe_status_t moe_layer(const moe_problem_t* p, const void* x, const float* logit
   if (e != hipSuccess) return MOE_ERR_HIP;
   GemmProblem gp;
   gp.R = M * p->topk;
-  gp.E = p->num_experts;
+  gp.E = held(p);
   gp.G = G;
   gp.offsets = offsets;
   gp.layer = 0;
@@ -310,7 +350,14 @@ moe_status_t moe_layer(const moe_problem_t* p, const void* x, const float* logit
   gp.N = p->hidden;
   e = p->dtype == MOE_DTYPE_BF16 ? launch_grouped_gemm_bf16(gp, s) : launch_grouped_gemm_f32(gp, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  return hip_status(launch_combine(y, w, f2s, M, p->hidden, p->topk, out, s));
+  return hip_status(launch_combine(y, w, f2s, M, p->hidden, p->topk, ep, s));
+}
+
+moe_status_t moe_layer(const moe_problem_t* p, const void* x, const float* logits, const int32_t* src_block,
+                       const void* w_gate, const void* w_up, const void* w_down, float* out,
+                       const moe_layer_aux_t* aux, const moe_layer_opts_t* opts, void* ws, size_t ws_bytes,
+                       void* stream) {
+  return moe_layer_ex(p, x, logits, src_block, w_gate, w_up, w_down, nullptr, out, aux, opts, ws, ws_bytes, stream);
 }
 
 moe_status_t moe_debug_device_status(const moe_problem_t* p, void* ws, size_t ws_bytes, void* stream) {

@@ -45,10 +45,12 @@ __device__ __forceinline__ float silu_mul_fast(float g, float u) {
 
 // Top-k weighted reduction of one 4-wide column group, shared by the
 // stand-alone combine and the fused layer so both give identical bits.
+// A slot whose row is -1 (a pair of an expert not held here) is left out.
 __device__ __forceinline__ float4 combine_group(const float* __restrict__ y, const float* __restrict__ w,
                                                 const int32_t* __restrict__ rows, int k, int64_t H, int64_t n) {
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int j = 0; j < k; ++j) {
+    if (rows[j] < 0) continue;
     const float wj = w[j];
     const float4 v = *reinterpret_cast<const float4*>(y + (int64_t)rows[j] * H + n);
     acc.x = fmaf(wj, v.x, acc.x);
@@ -57,6 +59,42 @@ __device__ __forceinline__ float4 combine_group(const float* __restrict__ y, con
     acc.w = fmaf(wj, v.w, acc.w);
   }
   return acc;
+}
+
+// Output epilogue of the combine: out = cast(acc + residual), one f32 add
+// (none without a residual), then f32 or bf16 (round to nearest even).
+struct OutEpilogue {
+  const void* residual;  // [M,H] bf16 or f32, or null
+  void* out;             // [M,H] f32 or bf16
+  int res_bf16;
+  int out_bf16;
+};
+
+// Stores the 4 values of out starting at element i (= t * H + n, i % 4 == 0).
+__device__ __forceinline__ void store_out(const OutEpilogue& ep, int64_t i, float4 acc) {
+  if (ep.residual) {
+    float4 r;
+    if (ep.res_bf16) {
+      const bf16x4_t b = *reinterpret_cast<const bf16x4_t*>(reinterpret_cast<const __bf16*>(ep.residual) + i);
+      r = make_float4((float)b[0], (float)b[1], (float)b[2], (float)b[3]);
+    } else {
+      r = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(ep.residual) + i);
+    }
+    acc.x += r.x;
+    acc.y += r.y;
+    acc.z += r.z;
+    acc.w += r.w;
+  }
+  if (ep.out_bf16) {
+    bf16x4_t o;
+    o[0] = (__bf16)acc.x;
+    o[1] = (__bf16)acc.y;
+    o[2] = (__bf16)acc.z;
+    o[3] = (__bf16)acc.w;
+    *reinterpret_cast<bf16x4_t*>(reinterpret_cast<__bf16*>(ep.out) + i) = o;
+  } else {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(ep.out) + i) = acc;
+  }
 }
 
 inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }

@@ -484,4 +484,20 @@ __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int
   }
 }
 
+// One row tile of a segment.  A segment of at most 128 rows (its only row
+// tile) runs as the 128-row variant: half the matrix-core work, the same k
+// order per element, so the same bits.  Longer segments' last tiles stay
+// full height: then every tile of a segment takes the same time, the tiles
+// running at once on an XCD stay in step and share the segment's weight
+// panels in its L2 (measured: halving those last tiles cost more in
+// re-read weights than it saved).
+template <int LAYER, bool GATHER = false>
+__device__ __forceinline__ void bf16_gemm_row_tile(const Bf16GemmArgs& p, int g, int seg_start, int seg_rows, int m0,
+                                                   int nt, char* __restrict__ lds) {
+  if (seg_rows <= kTileRows / 2)
+    bf16_gemm_tile<LAYER, GATHER, kTileRows / 2>(p, g, seg_start, seg_rows, m0, nt, lds);
+  else
+    bf16_gemm_tile<LAYER, GATHER>(p, g, seg_start, seg_rows, m0, nt, lds);
+}
+
 }  // namespace moe

@@ -76,7 +76,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(Bf16Gem
       for (int v = xcd_slot(blockIdx.x, grid); v < entries; v += grid) {
         if (v < tail0) {
           const TileCoord c = tile_coord(v, G, NT, kTileRows, group_cols, tl);
-          bf16_gemm_tile<LAYER>(args, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], c.m0, c.nt, lds);
+          bf16_gemm_row_tile<LAYER>(args, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], c.m0, c.nt, lds);
         } else {
           const int u = v - tail0, jj = u / s, ck = u - jj * s;
           const TileCoord c = tile_coord(tail0 + jj, G, NT, kTileRows, group_cols, tl);
@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(Bf16Gem
   for (int v = xcd_slot(blockIdx.x, grid); v < entries; v += grid) {
     if (v < T - half) {
       const TileCoord c = tile_coord(v, G, NT, kTileRows, group_cols, tl);
-      bf16_gemm_tile<LAYER>(args, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], c.m0, c.nt, lds);
+      bf16_gemm_row_tile<LAYER>(args, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], c.m0, c.nt, lds);
     } else {
       const int j = v - (T - half);
       const TileCoord c = tile_coord(T - half + j / 2, G, NT, kTileRows, group_cols, tl);

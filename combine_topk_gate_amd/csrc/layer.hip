@@ -164,7 +164,7 @@ __device__ void combine_chunk(const FusedArgs& a, int c, int64_t t0, int64_t t1,
       }
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        if (i0 + u < nt) *reinterpret_cast<float4*>(a.out + (t0 + i0 + u) * a.H + n) = o[u];
+        if (i0 + u < nt) store_out(a.out, (t0 + i0 + u) * a.H + n, o[u]);
     }
   }
   __syncthreads();
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(kGemmThreads) void fused_layer_kernel(FusedArgs a) 
       ga.c = a.hact;
       ga.K = a.H;
       ga.N = a.F;
-      bf16_gemm_tile<0, true>(ga, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], c.m0, c.nt, lds);
+      bf16_gemm_row_tile<0, true>(ga, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], c.m0, c.nt, lds);
       block_signal(l0done + c.mt, 1);
       continue;
     }
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(kGemmThreads) void fused_layer_kernel(FusedArgs a) 
       ga.c = a.y;
       ga.K = a.F;
       ga.N = a.H;
-      bf16_gemm_tile<1>(ga, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], c.m0, chunk * kChunkTiles + c.nt, lds);
+      bf16_gemm_row_tile<1>(ga, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], c.m0, chunk * kChunkTiles + c.nt, lds);
       block_signal(chunkdone + chunk, 1);
     } else if (comb_chunk >= 0) {
       if (!block_wait(chunkdone + comb_chunk, MT * chunk_width(comb_chunk), a.status, limit, &lds_word)) return;

@@ -24,7 +24,7 @@ struct FusedArgs {
   const int32_t* f2s;
   void* hact;
   float* y;
-  float* out;
+  OutEpilogue out;  // out, with the optional residual and its output type
   int32_t* status;
   int32_t* flags;
   int mt_max;  // M-tile bound the flag arrays are sized for

@@ -3,8 +3,12 @@
 // PTO MoE article (seven serial stages: local reorder by expert; the
 // count-as-flag paragraph: per-expert row counts) and COMET paper review
 // §4.1.2 (Layer0: order tokens by source first).  Pair f = t*k + j goes to
-// segment g = src_block[t] * E + topk_idx[t, j]; the sorted order lists the
-// segments in turn and, inside a segment, the pairs by increasing f.
+// segment g = src_block[t] * EL + (topk_idx[t, j] - base) when its expert is
+// one of the EL held here, and is dropped otherwise; the sorted order lists
+// the segments in turn and, inside a segment, the pairs by increasing f.
+// Dropped pairs are ranked as one more segment after the G reported ones,
+// so they take the sorted positions past the kept pairs; those positions
+// and the dropped pairs' flat_to_sorted entries are written as -1.
 //
 // No atomic operation decides an order, so every output is bit-exact and
 // independent of scheduling:
@@ -27,33 +31,39 @@ constexpr int kPermThreads = 256;
 constexpr int kPermWaves = kPermThreads / kWave;
 constexpr int kMaxSegments = 1024;
 
+// Segment of pair f; G (one past the reported segments) if dropped.
 __device__ __forceinline__ int seg_of(const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ src_block,
-                                      int E, int k, int64_t f) {
+                                      int ebase, int EL, int G, int k, int64_t f) {
   const int s = src_block ? src_block[f / k] : 0;
-  return s * E + topk_idx[f];
+  const unsigned e = (unsigned)(topk_idx[f] - ebase);
+  return e < (unsigned)EL ? s * EL + (int)e : G;
 }
 
+// Histograms over the Gi ranked segments (Gi = G, or G + 1 with dropped pairs).
 __global__ __launch_bounds__(kPermThreads) void seg_count_kernel(const int32_t* __restrict__ topk_idx,
-                                                                 const int32_t* __restrict__ src_block, int E, int k,
-                                                                 int64_t R, int G, int chunk,
+                                                                 const int32_t* __restrict__ src_block, int ebase,
+                                                                 int EL, int k, int64_t R, int G, int Gi, int chunk,
                                                                  int32_t* __restrict__ block_hist) {
   __shared__ int hist[kMaxSegments];
-  for (int g = threadIdx.x; g < G; g += kPermThreads) hist[g] = 0;
+  for (int g = threadIdx.x; g < Gi; g += kPermThreads) hist[g] = 0;
   __syncthreads();
   const int64_t begin = (int64_t)blockIdx.x * chunk;
   const int64_t end = (begin + chunk < R) ? begin + chunk : R;
   for (int64_t f = begin + threadIdx.x; f < end; f += kPermThreads)
-    atomicAdd(&hist[seg_of(topk_idx, src_block, E, k, f)], 1);
+    atomicAdd(&hist[seg_of(topk_idx, src_block, ebase, EL, G, k, f)], 1);
   __syncthreads();
-  for (int g = threadIdx.x; g < G; g += kPermThreads) block_hist[(int64_t)blockIdx.x * G + g] = hist[g];
+  for (int g = threadIdx.x; g < Gi; g += kPermThreads) block_hist[(int64_t)blockIdx.x * Gi + g] = hist[g];
 }
 
 // Column-wise exclusive scan of block_hist [blocks][G] (in place), the
 // per-segment totals (counts) and their exclusive scan (offsets).  Thread
 // layout: P = 1024 / G' threads per segment (G' = G rounded up to a power of
 // two), each owning a contiguous slice of the blocks, so every thread issues
-// independent loads and the chain of dependent adds stays short.
-__global__ __launch_bounds__(kMaxSegments) void seg_scan_kernel(int G, int blocks, int64_t R,
+// independent loads and the chain of dependent adds stays short.  Here G is
+// the number of ranked segments; the first Gr are reported: counts[0..Gr-1]
+// and offsets[0..Gr], where offsets[Gr] is the start of the dropped pairs'
+// segment when G > Gr, else R.
+__global__ __launch_bounds__(kMaxSegments) void seg_scan_kernel(int G, int Gr, int blocks, int64_t R,
                                                                 int32_t* __restrict__ block_hist,
                                                                 int32_t* __restrict__ counts,
                                                                 int32_t* __restrict__ offsets) {
@@ -84,7 +94,7 @@ __global__ __launch_bounds__(kMaxSegments) void seg_scan_kernel(int G, int block
   __syncthreads();
   const int total = (threadIdx.x < gp) ? s[threadIdx.x] : 0;
   if (threadIdx.x < gp) tot[threadIdx.x] = total;
-  if (threadIdx.x < G) counts[threadIdx.x] = total;
+  if (threadIdx.x < Gr) counts[threadIdx.x] = total;
   // exclusive scan of the totals over segments
   for (int off = 1; off < gp; off <<= 1) {
     const int v = (threadIdx.x < gp && threadIdx.x >= (unsigned)off) ? s[threadIdx.x - off] : 0;
@@ -92,8 +102,8 @@ __global__ __launch_bounds__(kMaxSegments) void seg_scan_kernel(int G, int block
     if (threadIdx.x < gp) s[threadIdx.x] += v;
     __syncthreads();
   }
-  if (threadIdx.x < G) offsets[threadIdx.x] = s[threadIdx.x] - total;
-  if (threadIdx.x == 0) offsets[G] = (int)R;
+  if (threadIdx.x < G && threadIdx.x <= Gr) offsets[threadIdx.x] = s[threadIdx.x] - total;
+  if (G == Gr && threadIdx.x == 0) offsets[Gr] = (int)R;
   __syncthreads();
   // block_hist[b][g] <- offsets[g] + pairs of segment g in blocks before b
   if (g < G) {
@@ -106,17 +116,19 @@ __global__ __launch_bounds__(kMaxSegments) void seg_scan_kernel(int G, int block
   }
 }
 
+// Ranks over the Gi ranked segments; a dropped pair (segment G) writes -1.
 __global__ __launch_bounds__(kPermThreads) void seg_rank_kernel(const int32_t* __restrict__ topk_idx,
-                                                                const int32_t* __restrict__ src_block, int E, int k,
-                                                                int64_t R, int G, int chunk, int nbits,
+                                                                const int32_t* __restrict__ src_block, int ebase,
+                                                                int EL, int k, int64_t R, int G, int Gi, int chunk,
+                                                                int nbits,
                                                                 const int32_t* __restrict__ block_base,
                                                                 int32_t* __restrict__ sorted_to_flat,
                                                                 int32_t* __restrict__ flat_to_sorted) {
   __shared__ int running[kMaxSegments];
   __shared__ int wcnt[kPermWaves][kMaxSegments];
   const int tid = threadIdx.x, w = tid / kWave;
-  for (int g = tid; g < G; g += kPermThreads) {
-    running[g] = block_base[(int64_t)blockIdx.x * G + g];
+  for (int g = tid; g < Gi; g += kPermThreads) {
+    running[g] = block_base[(int64_t)blockIdx.x * Gi + g];
 #pragma unroll
     for (int q = 0; q < kPermWaves; ++q) wcnt[q][g] = 0;
   }
@@ -127,7 +139,7 @@ __global__ __launch_bounds__(kPermThreads) void seg_rank_kernel(const int32_t* _
   for (int64_t base = begin; base < end; base += kPermThreads) {
     const int64_t f = base + tid;
     const bool valid = f < end;
-    const int g = valid ? seg_of(topk_idx, src_block, E, k, f) : 0;
+    const int g = valid ? seg_of(topk_idx, src_block, ebase, EL, G, k, f) : 0;
     uint64_t peers = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
       const int bit = (g >> b) & 1;
@@ -141,8 +153,9 @@ __global__ __launch_bounds__(kPermThreads) void seg_rank_kernel(const int32_t* _
     if (valid) {
       int pos = running[g] + rank;
       for (int q = 0; q < w; ++q) pos += wcnt[q][g];
-      sorted_to_flat[pos] = (int32_t)f;
-      flat_to_sorted[f] = pos;
+      const bool kept = g < G;
+      sorted_to_flat[pos] = kept ? (int32_t)f : -1;
+      flat_to_sorted[f] = kept ? pos : -1;
     }
     __syncthreads();
     if (valid && rank == 0) {
@@ -153,10 +166,13 @@ __global__ __launch_bounds__(kPermThreads) void seg_rank_kernel(const int32_t* _
   }
 }
 
-PermutePlan permute_plan(int64_t M, int k, int G) {
+PermutePlan permute_plan(int64_t M, int k, int S, int E, int base, int EL) {
   PermutePlan pl;
   pl.R = M * k;
-  pl.G = G;
+  pl.EL = EL > 0 ? EL : E;
+  pl.base = EL > 0 ? base : 0;
+  pl.G = S * pl.EL;
+  pl.Gi = pl.G + (pl.EL < E ? 1 : 0);
   // small chunks: many blocks rank in parallel (the ranking of one chunk is
   // sequential in steps of 256 pairs)
   int64_t chunk = 512;
@@ -167,19 +183,20 @@ PermutePlan permute_plan(int64_t M, int k, int G) {
   return pl;
 }
 
-size_t permute_ws_bytes(const PermutePlan& pl) { return (size_t)(pl.blocks > 0 ? pl.blocks : 1) * pl.G * 4; }
+size_t permute_ws_bytes(const PermutePlan& pl) { return (size_t)(pl.blocks > 0 ? pl.blocks : 1) * pl.Gi * 4; }
 
-hipError_t launch_permute(const PermutePlan& pl, const int32_t* topk_idx, const int32_t* src_block, int E, int k,
+hipError_t launch_permute(const PermutePlan& pl, const int32_t* topk_idx, const int32_t* src_block, int k,
                           int32_t* counts, int32_t* offsets, int32_t* sorted_to_flat, int32_t* flat_to_sorted,
                           int32_t* ws, hipStream_t s) {
   int nbits = 1;
-  while ((1 << nbits) < pl.G) ++nbits;
+  while ((1 << nbits) < pl.Gi) ++nbits;
   if (pl.blocks > 0)
-    seg_count_kernel<<<pl.blocks, kPermThreads, 0, s>>>(topk_idx, src_block, E, k, pl.R, pl.G, pl.chunk, ws);
-  seg_scan_kernel<<<1, kMaxSegments, 0, s>>>(pl.G, pl.blocks, pl.R, ws, counts, offsets);
+    seg_count_kernel<<<pl.blocks, kPermThreads, 0, s>>>(topk_idx, src_block, pl.base, pl.EL, k, pl.R, pl.G, pl.Gi,
+                                                        pl.chunk, ws);
+  seg_scan_kernel<<<1, kMaxSegments, 0, s>>>(pl.Gi, pl.G, pl.blocks, pl.R, ws, counts, offsets);
   if (pl.blocks > 0)
-    seg_rank_kernel<<<pl.blocks, kPermThreads, 0, s>>>(topk_idx, src_block, E, k, pl.R, pl.G, pl.chunk, nbits, ws,
-                                                       sorted_to_flat, flat_to_sorted);
+    seg_rank_kernel<<<pl.blocks, kPermThreads, 0, s>>>(topk_idx, src_block, pl.base, pl.EL, k, pl.R, pl.G, pl.Gi,
+                                                       pl.chunk, nbits, ws, sorted_to_flat, flat_to_sorted);
   return hipGetLastError();
 }
 
@@ -211,7 +228,9 @@ __global__ __launch_bounds__(kCopyThreads) void dispatch_copy_kernel(const u32x4
       for (int r = 0; r < kCopyRows; ++r) {
         if (r >= nr) break;
         for (int j = 0; j < k; ++j) {
-          u32x4_t* d = xp + (int64_t)f2s[(t0 + r) * k + j] * C;
+          const int32_t row = f2s[(t0 + r) * k + j];
+          if (row < 0) continue;  // pair of an expert not held here
+          u32x4_t* d = xp + (int64_t)row * C;
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const int c = c0 + u * kCopyThreads;

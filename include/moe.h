@@ -7,7 +7,8 @@
  *             stable permutation, gather of token rows sorted by segment
  *   grouped   Layer0: gate/up products + SwiGLU; Layer1: down product,
  *   GEMM      both as one grouped GEMM over all experts
- *   combine   top-k weighted reduction of each token's expert outputs
+ *   combine   top-k weighted reduction of each token's expert outputs,
+ *             optionally plus a residual and cast to bf16 (epilogue)
  *   layer     all of the above in one persistent kernel: one ordered work
  *             queue of Layer0 tiles, Layer1 tiles and combine items, with
  *             ready counters between them
@@ -22,7 +23,7 @@
  *            thread-block allocation from profiled metadata.
  *   [GGEMM]  "Grouped GEMM 为什么适合 MoE" (why grouped GEMM suits MoE):
  *            C_i = A_i B_i over G problems, tile queue, double buffering,
- *            L2 locality, fused epilogue.
+ *            L2 locality, fused epilogue (GemmAdd: Y = cast(Acc + Add)).
  *   [PTO]    "PTO MoE算子实战" (PTO MoE operator article): the seven serial
  *            stages (reorder, AllToAll, reorder, GMM1/SwiGLU/GMM2, reorder,
  *            AllToAllV, top-K weighted accumulation); MegaMoE fusion;
@@ -41,11 +42,14 @@
  *     logits must be finite, src_block values must lie in [0, S), topk_idx
  *     in [0, E), and offsets must be the exclusive prefix sum of the counts
  *     of the same call sequence.  Violating these is undefined behaviour.
- *   - Symbols: M tokens, H hidden, F expert width, E experts, k = topk,
- *     S source blocks, G = S*E segments, R = M*k routed rows.
- *   - Weight storage: W_gate, W_up stored [E,F,H] and W_down stored [E,H,F]:
- *     row f of W_gate[e] is column f of the H x F matrix of the math
- *     (x W_gate), so every stored row is contiguous in the reduction index.
+ *   - Symbols: M tokens, H hidden, F expert width, E experts routing
+ *     chooses from, EL experts held by the call (local_experts, = E unless
+ *     set), k = topk, S source blocks, G = S*EL segments, R = M*k routed
+ *     pairs (the capacity of every per-pair buffer).
+ *   - Weight storage: W_gate, W_up stored [EL,F,H] and W_down stored
+ *     [EL,H,F]: row f of W_gate[e] is column f of the H x F matrix of the
+ *     math (x W_gate), so every stored row is contiguous in the reduction
+ *     index.  Weight slot l holds expert expert_base + l.
  */
 #ifndef MOE_H_
 #define MOE_H_
@@ -73,20 +77,33 @@ typedef enum { MOE_OP_DISPATCH = 0, MOE_OP_GROUPED_GEMM = 1, MOE_OP_LAYER = 2 } 
 
 /*
  * Problem shape.  Limits: 0 <= M, M*k < 2^31; H and F multiples of 64 in
- * [64, 65536]; 1 <= E <= 512; 1 <= k <= min(E, 16); S >= 1, S*E <= 1024;
- * R*max(H,F) < 2^31 and E*H*F < 2^31 (32-bit element offsets).
+ * [64, 65536]; 1 <= E <= 512; 1 <= k <= min(E, 16); S >= 1; S*EL <= 1024
+ * (S*EL <= 1023 when EL < E); R*max(H,F) < 2^31 and EL*H*F < 2^31 (32-bit
+ * element offsets).
  * dtype is the type of x, the weights, X_perm and Hact: MOE_DTYPE_BF16
- * (fp32 accumulation) or MOE_DTYPE_F32.  Logits, weights of the top-k, Y and
- * out are always f32.
+ * (fp32 accumulation) or MOE_DTYPE_F32.  Logits, weights of the top-k and Y
+ * are always f32; out is f32 unless an epilogue asks for bf16.
+ *
+ * Local experts ([COMET] §4.1.2 tokens grouped by source and expert for
+ * expert parallelism; [PTO] measured case: 16 local experts per card, the
+ * rest on other cards): routing chooses among all E experts; a call with
+ * local_experts = EL > 0 holds experts [expert_base, expert_base + EL) and
+ * keeps only the pairs routed to them.  Kept pair f goes to segment
+ * src * EL + (expert - expert_base); the other pairs are dropped, and the
+ * combine's out is this call's share of each token's sum (the partial
+ * combine that the holders of the other experts complete).  local_experts =
+ * 0 (or E with expert_base 0) is the plain layer.
  */
 typedef struct {
   int64_t num_tokens;     /* M */
   int32_t hidden;         /* H */
   int32_t ffn;            /* F */
-  int32_t num_experts;    /* E */
+  int32_t num_experts;    /* E: experts routing chooses from */
   int32_t topk;           /* k */
   int32_t num_src_blocks; /* S (1 unless rows arrive tagged by source block) */
   int32_t dtype;          /* moe_dtype_t */
+  int32_t expert_base;    /* first expert held (0 unless local_experts > 0) */
+  int32_t local_experts;  /* EL: experts held, expert_base + EL <= E; 0 = all E */
 } moe_problem_t;
 
 /* Bytes of device workspace `op` needs for this problem (0 if none).
@@ -109,13 +126,17 @@ moe_status_t moe_route(const moe_problem_t* p, const float* logits, int32_t* top
 /*
  * Dispatch ([PTO] local reorder by expert + count-as-flag counts; [COMET]
  * §4.1.2 reorder by source; §3.2 Layer0 dispatch).  Pair f = t*k + j belongs
- * to segment g = src_block[t]*E + topk_idx[t,j] (src_block NULL means S = 1).
+ * to segment g = src_block[t]*EL + (topk_idx[t,j] - expert_base) if that
+ * expert is held, else it is dropped (src_block NULL means S = 1).
  *   counts[g]          number of pairs in segment g                 [G] int32
- *   offsets            exclusive prefix sum of counts, offsets[G]=R [G+1] int32
+ *   offsets            exclusive prefix sum of counts; offsets[G] = the
+ *                      number of kept pairs (R when all are held)   [G+1] int32
  *   sorted_to_flat[r]  the pair at sorted position r: segments in order,
- *                      increasing f inside a segment (stable)       [R] int32
- *   flat_to_sorted     the inverse permutation                     [R] int32
- *   x_perm[r, :]       = x[sorted_to_flat[r] / k, :]  (byte copy)   [R,H] dtype
+ *                      increasing f inside a segment (stable); -1 for
+ *                      r >= offsets[G]                              [R] int32
+ *   flat_to_sorted     the inverse permutation; -1 for a dropped pair [R] int32
+ *   x_perm[r, :]       = x[sorted_to_flat[r] / k, :]  (byte copy) for
+ *                      r < offsets[G]; later rows are not written   [R,H] dtype
  *   x                  [M,H] dtype, read only
  * Results are bit-exact and independent of scheduling (no atomics decide
  * an order).  ws must hold moe_workspace_bytes(p, MOE_OP_DISPATCH) bytes.
@@ -126,14 +147,15 @@ moe_status_t moe_dispatch(const moe_problem_t* p, const void* x, const int32_t* 
 
 /*
  * Grouped GEMM over the G segments ([GGEMM] C_i = A_i B_i with per-problem
- * sizes; segment g uses expert g % E and rows offsets[g] .. offsets[g+1]-1).
+ * sizes; segment g uses weight slot g % EL and rows offsets[g] ..
+ * offsets[g+1]-1; rows from offsets[G] on are neither read nor written).
  *   layer 0 ([COMET] §3.2 Layer0; [PTO] GMM1 -> SwiGLU):
- *     a  = X_perm [R,H] dtype; w0 = W_gate [E,F,H]; w1 = W_up [E,F,H]
+ *     a  = X_perm [R,H] dtype; w0 = W_gate [EL,F,H]; w1 = W_up [EL,F,H]
  *     c  = Hact [R,F] dtype: Hact[r,f] = silu(g) * u rounded to dtype, where
  *          g = sum_h X_perm[r,h] W_gate[e,f,h], u likewise with W_up, both
  *          accumulated in f32, silu(z) = z / (1 + exp(-z)).
  *   layer 1 ([COMET] §3.2 Layer1; [PTO] GMM2):
- *     a  = Hact [R,F] dtype; w0 = W_down [E,H,F]; w1 = NULL
+ *     a  = Hact [R,F] dtype; w0 = W_down [EL,H,F]; w1 = NULL
  *     c  = Y [R,H] f32: Y[r,n] = sum_f Hact[r,f] W_down[e,n,f], f32 accumulation.
  *   offsets [G+1] int32 as produced by moe_dispatch.  Rows of empty segments
  *   produce nothing.
@@ -155,11 +177,32 @@ moe_status_t moe_grouped_gemm(const moe_problem_t* p, int32_t layer, const void*
  * Combine ([COMET] §4.1.1/§4.1.2 Top-K reduction, column-wise; [PTO] Combine
  * + Unpermute, top-K weighted accumulation).
  *   out[t, n] = sum_{j=0..k-1} topk_w[t,j] * y[flat_to_sorted[t*k+j], n],
- *   f32, accumulated from zero in slot order j = 0..k-1 (fused multiply-add).
+ *   f32, accumulated from zero in slot order j = 0..k-1 (fused multiply-add);
+ *   slots whose flat_to_sorted is -1 (pairs of experts not held) are left
+ *   out, so a token with none of them gets 0.
  *   y [R,H] f32; topk_w [M,k] f32; flat_to_sorted [R] int32; out [M,H] f32.
  */
 moe_status_t moe_combine(const moe_problem_t* p, const float* y, const float* topk_w, const int32_t* flat_to_sorted,
                          float* out, void* stream);
+
+/*
+ * Output epilogue of the combine ([GGEMM] fused GemmAdd epilogue, Y =
+ * cast(Acc + Add)): acc is the combine's f32 sum above; then
+ *   out[t, n] = cast(acc[t, n] + residual[t, n])
+ * with one f32 addition (no residual: acc itself) and the cast to out_dtype:
+ * f32 keeps the value, bf16 rounds to nearest even.
+ *   residual  [M,H] in the problem's dtype (bf16 or f32), or NULL
+ *   out_dtype MOE_DTYPE_F32 or MOE_DTYPE_BF16
+ */
+typedef struct {
+  const void* residual;
+  int32_t out_dtype;
+} moe_epilogue_t;
+
+/* moe_combine with an epilogue (NULL epi: as moe_combine); out [M,H] in
+ * epi->out_dtype, 16-byte aligned; residual 16-byte aligned. */
+moe_status_t moe_combine_ex(const moe_problem_t* p, const float* y, const float* topk_w,
+                            const int32_t* flat_to_sorted, const moe_epilogue_t* epi, void* out, void* stream);
 
 /* Optional device buffers that receive moe_layer's intermediates (any field
  * may be NULL, then the workspace holds that intermediate). */
@@ -203,7 +246,8 @@ typedef struct {
  * own chain passes one (the last round split along k, see
  * moe_grouped_gemm), which regroups the k sum of those tiles only.
  *   x [M,H] dtype; logits [M,E] f32; src_block [M] int32 or NULL (S = 1);
- *   w_gate, w_up [E,F,H]; w_down [E,H,F]; out [M,H] f32.
+ *   w_gate, w_up [EL,F,H]; w_down [EL,H,F]; out [M,H] f32 (the partial
+ *   combine when EL < E).
  *   aux: the fused path writes X_perm only if aux->x_perm is given.
  * The fused kernel needs its whole grid resident (one workgroup per CU):
  * opts->grid above that returns MOE_ERR_UNSUPPORTED; n_mover >= grid returns
@@ -215,6 +259,14 @@ moe_status_t moe_layer(const moe_problem_t* p, const void* x, const float* logit
                        const void* w_gate, const void* w_up, const void* w_down, float* out,
                        const moe_layer_aux_t* aux, const moe_layer_opts_t* opts, void* ws, size_t ws_bytes,
                        void* stream);
+
+/* moe_layer with the combine's epilogue (NULL epi: as moe_layer); out [M,H]
+ * in epi->out_dtype.  The fused kernel and the chain apply it in the same
+ * f32 order, so they still agree bit for bit. */
+moe_status_t moe_layer_ex(const moe_problem_t* p, const void* x, const float* logits, const int32_t* src_block,
+                          const void* w_gate, const void* w_up, const void* w_down, const moe_epilogue_t* epi,
+                          void* out, const moe_layer_aux_t* aux, const moe_layer_opts_t* opts, void* ws,
+                          size_t ws_bytes, void* stream);
 
 /* The plan the profiled split table picks for this problem (what moe_layer
  * does when opts->n_mover < 0): the number of dedicated combine workgroups

@@ -16,6 +16,13 @@ experts, 2048 tokens per source):
     mixtral   8192   4096  14336  8   2  1  bf16   0.032
     phi35     16384  4096  6400   16  2  1  bf16   0.05
     epshare   16384  7168  4096   16  8  8  bf16   0  (8 source blocks x 2048 rows)
+    epshare_b 16384  7168  4096  128  8  8  bf16   0  (same blocks; experts 0..15 held)
+
+The two expert-parallel readings of the PTO measured case: in epshare the 8
+source blocks are routed among the 16 local experts only; in epshare_b they
+are routed among 8 x 16 = 128 experts (one group of 16 per card) and this
+call holds experts 0..15, so it keeps about 1/8 of the routed pairs (about
+1024 per held expert) and its combine is the partial one.
 
 Distributions: x ~ N(0,1); gate logits ~ N(0,1) in f32 plus, for the skewed
 layers, a per-expert bias s * z_e (z drawn N(0,1), then standardised) whose
@@ -66,6 +73,12 @@ class Config:
     seed: int = 0
     skew: float = 0.0
     block: int = 0  # tokens per source block (S > 1)
+    base: int = 0   # first expert held
+    local: int = 0  # experts held (0: all E); the weights hold these only
+
+    @property
+    def EL(self) -> int:
+        return self.local if self.local else self.E
 
     @property
     def R(self) -> int:
@@ -83,6 +96,7 @@ CONFIGS = {
     "mixtral": Config("mixtral", 8192, 4096, 14336, 8, 2, 1, "bf16", 103, 0.032),
     "phi35": Config("phi35", 16384, 4096, 6400, 16, 2, 1, "bf16", 104, 0.05),
     "epshare": Config("epshare", 16384, 7168, 4096, 16, 8, 8, "bf16", 105, 0.0, 2048),
+    "epshare_b": Config("epshare_b", 16384, 7168, 4096, 128, 8, 8, "bf16", 106, 0.0, 2048, 0, 16),
 }
 
 
@@ -162,20 +176,23 @@ def _weight(cfg: Config, tag: int, e: int, rows: int, cols: int) -> np.ndarray:
 
 
 def make_weights(cfg: Config, threads: int = 8):
-    """(W_gate [E,F,H], W_up [E,F,H], W_down [E,H,F])."""
+    """(W_gate [EL,F,H], W_up [EL,F,H], W_down [EL,H,F]) of the held experts
+    base .. base + EL - 1 (each drawn from its expert's own stream, so a
+    held slice equals the same slice of the full stack)."""
     dt = np.float32 if cfg.dtype == "f32" else np.uint16
-    wg = np.empty((cfg.E, cfg.F, cfg.H), dt)
-    wu = np.empty((cfg.E, cfg.F, cfg.H), dt)
-    wd = np.empty((cfg.E, cfg.H, cfg.F), dt)
+    EL = cfg.EL
+    wg = np.empty((EL, cfg.F, cfg.H), dt)
+    wu = np.empty((EL, cfg.F, cfg.H), dt)
+    wd = np.empty((EL, cfg.H, cfg.F), dt)
     jobs = []
-    for e in range(cfg.E):
-        jobs.append((wg, _T_WG, e, cfg.F, cfg.H))
-        jobs.append((wu, _T_WU, e, cfg.F, cfg.H))
-        jobs.append((wd, _T_WD, e, cfg.H, cfg.F))
+    for slot in range(EL):
+        jobs.append((wg, _T_WG, slot, cfg.F, cfg.H))
+        jobs.append((wu, _T_WU, slot, cfg.F, cfg.H))
+        jobs.append((wd, _T_WD, slot, cfg.H, cfg.F))
 
     def run(job):
-        dst, tag, e, r, c = job
-        dst[e] = _weight(cfg, tag, e, r, c)
+        dst, tag, slot, r, c = job
+        dst[slot] = _weight(cfg, tag, cfg.base + slot, r, c)
 
     with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
         list(ex.map(run, jobs))

@@ -26,7 +26,7 @@ def host(t):
 
 
 def problem_of(cfg):
-    return moe.problem(cfg.M, cfg.H, cfg.F, cfg.E, cfg.k, cfg.S, cfg.dtype)
+    return moe.problem(cfg.M, cfg.H, cfg.F, cfg.E, cfg.k, cfg.S, cfg.dtype, cfg.base, cfg.local)
 
 
 def upload(d, device="cuda:0"):
@@ -40,7 +40,7 @@ def run_chain(cfg, g, device="cuda:0", gemm_ws=True):
     then split along k, as in moe_layer's chain); without it the GEMM runs
     unsplit, which is what the fused kernel reproduces bit for bit."""
     p = problem_of(cfg)
-    M, k, H, F, G, R = cfg.M, cfg.k, cfg.H, cfg.F, cfg.S * cfg.E, cfg.M * cfg.k
+    M, k, H, F, G, R = cfg.M, cfg.k, cfg.H, cfg.F, cfg.S * cfg.EL, cfg.M * cfg.k
     act = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     o = dict(
         topk_idx=torch.empty((M, k), dtype=torch.int32, device=device),
@@ -49,9 +49,10 @@ def run_chain(cfg, g, device="cuda:0", gemm_ws=True):
         offsets=torch.empty(G + 1, dtype=torch.int32, device=device),
         sorted_to_flat=torch.empty(R, dtype=torch.int32, device=device),
         flat_to_sorted=torch.empty(R, dtype=torch.int32, device=device),
-        x_perm=torch.empty((R, H), dtype=act, device=device),
-        hact=torch.empty((R, F), dtype=act, device=device),
-        y=torch.empty((R, H), dtype=torch.float32, device=device),
+        # zeroed: rows past the kept pairs (experts not held) are never written
+        x_perm=torch.zeros((R, H), dtype=act, device=device),
+        hact=torch.zeros((R, F), dtype=act, device=device),
+        y=torch.zeros((R, H), dtype=torch.float32, device=device),
         out=torch.empty((M, H), dtype=torch.float32, device=device),
     )
     ws = torch.empty(max(moe.moe_workspace_bytes(p, moe.MOE_OP_DISPATCH), 4), dtype=torch.uint8, device=device)
@@ -76,7 +77,7 @@ def layer_runs_chain(cfg):
 
 def run_layer(cfg, g, device="cuda:0", aux=False, **opts):
     p = problem_of(cfg)
-    M, k, H, F, G, R = cfg.M, cfg.k, cfg.H, cfg.F, cfg.S * cfg.E, cfg.M * cfg.k
+    M, k, H, F, G, R = cfg.M, cfg.k, cfg.H, cfg.F, cfg.S * cfg.EL, cfg.M * cfg.k
     ws = torch.empty(moe.moe_workspace_bytes(p, moe.MOE_OP_LAYER), dtype=torch.uint8, device=device)
     out = torch.empty((M, H), dtype=torch.float32, device=device)
     a = None
@@ -89,9 +90,9 @@ def run_layer(cfg, g, device="cuda:0", aux=False, **opts):
             offsets=torch.empty(G + 1, dtype=torch.int32, device=device),
             sorted_to_flat=torch.empty(R, dtype=torch.int32, device=device),
             flat_to_sorted=torch.empty(R, dtype=torch.int32, device=device),
-            x_perm=torch.empty((R, H), dtype=act, device=device),
-            hact=torch.empty((R, F), dtype=act, device=device),
-            y=torch.empty((R, H), dtype=torch.float32, device=device),
+            x_perm=torch.zeros((R, H), dtype=act, device=device),
+            hact=torch.zeros((R, F), dtype=act, device=device),
+            y=torch.zeros((R, H), dtype=torch.float32, device=device),
         )
     moe.moe_layer(p, g["x"], g["logits"], g.get("src_block"), g["w_gate"], g["w_up"], g["w_down"], out, ws, aux=a,
                   **opts)

@@ -46,7 +46,7 @@ def test_no_torch_types_in_header():
 
 
 def test_version_and_status_strings(lib):
-    assert moe.moe_abi_version() >> 16 == 1
+    assert moe.moe_abi_version() >> 16 == 2
     assert moe.moe_status_string(moe.MOE_OK) == "MOE_OK"
     assert moe.moe_status_string(moe.MOE_ERR_DEVICE_TIMEOUT) == "MOE_ERR_DEVICE_TIMEOUT"
 
@@ -54,14 +54,18 @@ def test_version_and_status_strings(lib):
 BAD = [
     dict(M=-1), dict(H=100), dict(H=0), dict(F=32), dict(E=0), dict(E=513), dict(k=0), dict(k=17),
     dict(E=4, k=5), dict(S=0), dict(S=3, E=512), dict(dtype=7),
+    # held experts: negative, base without a count, past E, too many segments with the dropped one
+    dict(EL=-1), dict(base=-1, EL=2), dict(base=3, EL=0), dict(base=6, EL=3), dict(E=512, S=4, EL=256),
+    dict(E=512, S=3, EL=512),
 ]
 
 
 @pytest.mark.parametrize("bad", BAD)
 def test_invalid_problem_is_rejected_without_launch(lib, bad):
-    shape = dict(M=16, H=64, F=64, E=8, k=2, S=1, dtype=moe.MOE_DTYPE_BF16)
+    shape = dict(M=16, H=64, F=64, E=8, k=2, S=1, dtype=moe.MOE_DTYPE_BF16, base=0, EL=0)
     shape.update(bad)
-    p = moe.Problem(shape["M"], shape["H"], shape["F"], shape["E"], shape["k"], shape["S"], shape["dtype"])
+    p = moe.Problem(shape["M"], shape["H"], shape["F"], shape["E"], shape["k"], shape["S"], shape["dtype"],
+                    shape["base"], shape["EL"])
     assert lib.moe_route(ctypes.byref(p), None, None, None, None) == moe.MOE_ERR_INVALID_ARGUMENT
     assert lib.moe_workspace_bytes(ctypes.byref(p), moe.MOE_OP_LAYER) == 0
     assert lib.moe_layer_default_movers(ctypes.byref(p)) == -1
@@ -94,6 +98,40 @@ def test_null_and_misaligned_pointers_are_rejected(lib):
     r = lib.moe_layer(ctypes.byref(p), fake, fake, None, fake, fake, fake, fake, None, ctypes.byref(opts), ws, 16,
                       None)
     assert r == moe.MOE_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_held_experts_limits(lib):
+    # S * EL = 1024 is fine when every expert is held; with one not held the
+    # dropped pairs need one more segment
+    assert lib.moe_workspace_bytes(ctypes.byref(moe.problem(16, 64, 64, 512, 2, S=2)), moe.MOE_OP_LAYER) > 0
+    assert lib.moe_workspace_bytes(ctypes.byref(moe.problem(16, 64, 64, 512, 2, S=4, local_experts=256)),
+                                   moe.MOE_OP_LAYER) == 0
+    assert lib.moe_workspace_bytes(ctypes.byref(moe.problem(16, 64, 64, 512, 2, S=4, expert_base=1,
+                                                            local_experts=255)), moe.MOE_OP_LAYER) > 0
+    # EL = E with base 0 is the plain problem: same workspace
+    a = moe.problem(300, 128, 256, 16, 4, S=2)
+    b = moe.problem(300, 128, 256, 16, 4, S=2, local_experts=16)
+    for op in (moe.MOE_OP_DISPATCH, moe.MOE_OP_GROUPED_GEMM, moe.MOE_OP_LAYER):
+        assert lib.moe_workspace_bytes(ctypes.byref(a), op) == lib.moe_workspace_bytes(ctypes.byref(b), op)
+
+
+def test_bad_epilogue_is_rejected(lib):
+    p = moe.problem(16, 64, 64, 8, 2)
+    fake, odd = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1008)
+    bad_type = moe.Epilogue(None, 7)
+    assert lib.moe_combine_ex(ctypes.byref(p), fake, fake, fake, ctypes.byref(bad_type), fake, None) == \
+        moe.MOE_ERR_INVALID_ARGUMENT
+    odd_res = moe.Epilogue(odd, moe.MOE_DTYPE_BF16)
+    assert lib.moe_combine_ex(ctypes.byref(p), fake, fake, fake, ctypes.byref(odd_res), fake, None) == \
+        moe.MOE_ERR_INVALID_ARGUMENT
+    ok = moe.Epilogue(None, moe.MOE_DTYPE_BF16)
+    assert lib.moe_combine_ex(ctypes.byref(p), fake, fake, fake, ctypes.byref(ok), odd, None) == \
+        moe.MOE_ERR_INVALID_ARGUMENT
+    opts = moe.LayerOpts(-1, 0, 1, 0)
+    ws = ctypes.c_void_p(0x100000)
+    r = lib.moe_layer_ex(ctypes.byref(p), fake, fake, None, fake, fake, fake, ctypes.byref(bad_type), fake, None,
+                         ctypes.byref(opts), ws, 1 << 30, None)
+    assert r == moe.MOE_ERR_INVALID_ARGUMENT
 
 
 def test_unsupported_sizes(lib):

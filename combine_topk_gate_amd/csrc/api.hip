@@ -218,7 +218,7 @@ moe_status_t moe_combine(const moe_problem_t* p, const float* y, const float* to
 int32_t moe_layer_default_movers(const moe_problem_t* p) {
   if (check_problem(p) != MOE_OK || p->dtype != MOE_DTYPE_BF16) return -1;
   return fused_default_movers(p->num_tokens, p->hidden, p->ffn, p->num_experts, p->topk, p->num_src_blocks,
-                              p->dtype, device_cu_count());
+                              held(p), p->dtype, device_cu_count());
 }
 
 moe_status_t moe_layer_ex(const moe_problem_t* p, const void* x, const float* logits, const int32_t* src_block,
@@ -286,7 +286,7 @@ moe_status_t moe_layer_ex(const moe_problem_t* p, const void* x, const float* lo
   // n_mover < 0 asks the profiled table, which may pick the kernel chain
   const int movers = o.n_mover >= 0 ? o.n_mover
                                     : fused_default_movers(M, p->hidden, p->ffn, p->num_experts, p->topk,
-                                                           p->num_src_blocks, p->dtype, cus);
+                                                           p->num_src_blocks, held(p), p->dtype, cus);
   const bool fused = o.fused != 0 && p->dtype == MOE_DTYPE_BF16 && movers >= 0;
   if (fused) {
     FusedArgs fa;

@@ -35,7 +35,8 @@ struct FusedArgs {
 
 size_t fused_ws_bytes(int64_t M, int H, int F, int E, int k, int S);
 int fused_mt_max(int64_t M, int H, int k, int G);
-int fused_default_movers(int64_t M, int H, int F, int E, int k, int S, int dtype, int cus);
+// EL: experts held (E when all are).
+int fused_default_movers(int64_t M, int H, int F, int E, int k, int S, int EL, int dtype, int cus);
 moe_status_t fused_check(const FusedArgs& a, int cus);
 hipError_t launch_fused_layer(const FusedArgs& a, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);

@@ -78,6 +78,7 @@ __global__ __launch_bounds__(kMaxSegments) void seg_scan_kernel(int G, int Gr, i
   const int b0 = p * L, b1 = min(blocks, b0 + L);
   int sum = 0;
   if (g < G)
+#pragma unroll 8
     for (int b = b0; b < b1; ++b) sum += block_hist[(int64_t)b * G + g];
   part[threadIdx.x] = sum;
   __syncthreads();
@@ -108,6 +109,7 @@ __global__ __launch_bounds__(kMaxSegments) void seg_scan_kernel(int G, int Gr, i
   // block_hist[b][g] <- offsets[g] + pairs of segment g in blocks before b
   if (g < G) {
     int run = s[g] - tot[g] + part[threadIdx.x];  // offsets[g] + blocks before this slice
+#pragma unroll 8
     for (int b = b0; b < b1; ++b) {
       const int v = block_hist[(int64_t)b * G + g];
       block_hist[(int64_t)b * G + g] = run;
@@ -215,6 +217,14 @@ __global__ __launch_bounds__(kCopyThreads) void dispatch_copy_kernel(const u32x4
                                                                      u32x4_t* __restrict__ xp) {
   for (int64_t t0 = (int64_t)blockIdx.x * kCopyRows; t0 < M; t0 += (int64_t)gridDim.x * kCopyRows) {
     const int nr = (M - t0) < kCopyRows ? (int)(M - t0) : kCopyRows;
+    // a token none of whose pairs is held here is not read at all
+    bool need[kCopyRows];
+#pragma unroll
+    for (int r = 0; r < kCopyRows; ++r) {
+      need[r] = false;
+      if (r < nr)
+        for (int j = 0; j < k; ++j) need[r] |= f2s[(t0 + r) * k + j] >= 0;
+    }
     for (int c0 = threadIdx.x; c0 < C; c0 += kCopyThreads * 2) {
       u32x4_t v[kCopyRows][2];
 #pragma unroll
@@ -222,11 +232,11 @@ __global__ __launch_bounds__(kCopyThreads) void dispatch_copy_kernel(const u32x4
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int c = c0 + u * kCopyThreads;
-          if (r < nr && c < C) v[r][u] = x[(t0 + r) * C + c];
+          if (need[r] && c < C) v[r][u] = x[(t0 + r) * C + c];
         }
 #pragma unroll
       for (int r = 0; r < kCopyRows; ++r) {
-        if (r >= nr) break;
+        if (r >= nr || !need[r]) continue;
         for (int j = 0; j < k; ++j) {
           const int32_t row = f2s[(t0 + r) * k + j];
           if (row < 0) continue;  // pair of an expert not held here

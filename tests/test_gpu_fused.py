@@ -89,9 +89,9 @@ def test_unfused_option_equals_chain(qwen):
 
 
 def test_default_split_comes_from_table():
-    for name in ("qwen2", "mixtral", "phi35", "epshare"):
+    for name in ("qwen2", "mixtral", "phi35", "epshare", "epshare_b"):
         c = moe_synth.config(name)
-        m = moe.moe_layer_default_movers(moe.problem(c.M, c.H, c.F, c.E, c.k, c.S, c.dtype))
+        m = moe.moe_layer_default_movers(moe.problem(c.M, c.H, c.F, c.E, c.k, c.S, c.dtype, c.base, c.local))
         assert -1 <= m < 64, (name, m)
     assert moe.moe_layer_default_movers(moe.problem(256, 256, 512, 8, 2, 1, "f32")) == -1
 

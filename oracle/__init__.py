@@ -46,14 +46,21 @@ def _configure(lib):
     lib.orc_counts_offsets.argtypes = [I64, I32, I32, I32, I32, I32, P, P, P, P]
     lib.orc_permutation.argtypes = [I64, I32, I32, I32, I32, I32, P, P, P, P]
     lib.orc_dispatch.argtypes = [I64, I32, I32, I32, P, P, P]
-    lib.orc_ffn_rows.argtypes = [I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, I64, P, P, P]
+    lib.orc_ffn_rows.argtypes = [I32, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, I64, P, P, P]
+    lib.orc_e4m3_value.argtypes = [ctypes.c_uint8]
+    lib.orc_e4m3_value.restype = ctypes.c_double
+    lib.orc_e4m3_round.argtypes = [ctypes.c_double]
+    lib.orc_e4m3_round.restype = ctypes.c_uint8
+    lib.orc_mx_quantize.argtypes = [I64, I32, I32, P, P]
+    lib.orc_mx_dequantize.argtypes = [I64, I32, P, P]
     lib.orc_combine_tokens.argtypes = [I32, I32, I64, P, P, P, P]
     lib.orc_epilogue.argtypes = [I64, P, P, I32, I32, P]
-    lib.orc_moe_layer.argtypes = [I64, I32, I32, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, I64, P,
+    lib.orc_moe_layer.argtypes = [I64, I32, I32, I32, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, I64, P,
                                   P, P, P, P, P, P, P, P, P]
     lib.orc_num_threads.argtypes = []
     for name in ("orc_route", "orc_counts_offsets", "orc_permutation", "orc_dispatch",
-                 "orc_ffn_rows", "orc_combine_tokens", "orc_epilogue", "orc_moe_layer", "orc_num_threads"):
+                 "orc_ffn_rows", "orc_combine_tokens", "orc_epilogue", "orc_moe_layer", "orc_num_threads",
+                 "orc_mx_quantize", "orc_mx_dequantize"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -183,6 +190,36 @@ def dispatch(x, k, sorted_to_flat):
     return xp
 
 
+def e4m3_value(code: int) -> float:
+    """Value of an e4m3 code (OCP 8-bit "fn" variant)."""
+    return _load().orc_e4m3_value(int(code))
+
+
+def e4m3_round(v: float) -> int:
+    """Nearest e4m3 code (ties to the even code, clamped to +-448)."""
+    return int(_load().orc_e4m3_round(float(v)))
+
+
+def mx_quantize(values):
+    """MXFP8 quantisation of a [rows, cols] array (f32, bf16 bits or f64;
+    cols a multiple of 32) in blocks of 32 along a row: one uint8 buffer of
+    rows*cols e4m3 codes followed by rows*cols/32 scale bytes."""
+    v = np.ascontiguousarray(values)
+    rows, cols = v.shape[0], int(np.prod(v.shape[1:]))
+    dt = -1 if v.dtype == np.float64 else _dtype_code(v)
+    out = np.empty(rows * cols + rows * cols // 32, np.uint8)
+    _check(_load().orc_mx_quantize(rows, cols, dt, _p(v), _p(out)), "mx_quantize")
+    return out
+
+
+def mx_dequantize(buf, rows, cols):
+    """Values of an MXFP8 buffer as float64 [rows, cols]."""
+    b = _c(buf, np.uint8)
+    out = np.empty((rows, cols), np.float64)
+    _check(_load().orc_mx_dequantize(rows, cols, _p(b), _p(out)), "mx_dequantize")
+    return out
+
+
 def ffn_rows(x, w_gate, w_up, w_down, k, S, sorted_to_flat, offsets, rows):
     """Steps 5-6 for the listed sorted rows: (hact [n,F], y [n,H]) in float64."""
     x = np.ascontiguousarray(x)
@@ -193,7 +230,7 @@ def ffn_rows(x, w_gate, w_up, w_down, k, S, sorted_to_flat, offsets, rows):
     n = rows.shape[0]
     hact = np.empty((n, F), np.float64)
     y = np.empty((n, H), np.float64)
-    _check(_load().orc_ffn_rows(H, F, E, S, k, dt, _p(x), _p(wg), _p(wu), _p(wd),
+    _check(_load().orc_ffn_rows(H, F, E, S, k, dt, 0, _p(x), _p(wg), _p(wu), _p(wd),
                                 _p(_c(sorted_to_flat, np.int32)), _p(_c(offsets, np.int32)), n, _p(rows),
                                 _p(hact), _p(y)), "ffn_rows")
     return hact, y
@@ -228,7 +265,7 @@ def epilogue(acc, residual=None, out_dtype="f32"):
 
 
 def moe_layer(x, logits, w_gate, w_up, w_down, k, S=1, src_block=None, tokens=None, want_rows=False,
-              expert_base=0, local_experts=0, residual=None, out_dtype="f32"):
+              expert_base=0, local_experts=0, residual=None, out_dtype="f32", w_down_mx=None):
     """The whole layer.  Routing, counts, offsets and the permutation are
     computed for every token; the FFN and the combine for ``tokens`` only
     (all tokens if None).  Routing chooses among logits.shape[1] experts;
@@ -236,7 +273,9 @@ def moe_layer(x, logits, w_gate, w_up, w_down, k, S=1, src_block=None, tokens=No
     [expert_base, expert_base + EL) only and out is the partial combine over
     the pairs routed to them.  residual [M,H] and out_dtype select the
     epilogue cast(acc + residual) ("out" then holds its values; "acc" the
-    plain combine).  Returns a dict of numpy arrays."""
+    plain combine).  w_down_mx (an mx_quantize buffer of W_down) selects
+    the MXFP8 activation path: Hact quantised in blocks of 32 along F and the
+    down product on the quantised values.  Returns a dict of numpy arrays."""
     x = np.ascontiguousarray(x)
     dt = _dtype_code(x)
     logits = _c(logits, np.float32)
@@ -246,6 +285,11 @@ def moe_layer(x, logits, w_gate, w_up, w_down, k, S=1, src_block=None, tokens=No
     assert H2 == H and logits.shape == (M, E)
     assert EL == _local(E, expert_base, local_experts)
     wg, wu, wd = (np.ascontiguousarray(a, dtype=x.dtype) for a in (w_gate, w_up, w_down))
+    act_fp8 = 0
+    if w_down_mx is not None:
+        act_fp8 = 1
+        wd = _c(w_down_mx, np.uint8)
+        assert wd.size == EL * H * F + EL * H * F // 32
     src_block = _c(src_block, np.int32)
     tok = None if tokens is None else _c(tokens, np.int64)
     n_tok = M if tok is None else tok.shape[0]
@@ -256,7 +300,7 @@ def moe_layer(x, logits, w_gate, w_up, w_down, k, S=1, src_block=None, tokens=No
         out=np.empty((n_tok, H), np.float64))
     hact = np.empty((n_tok * k, F), np.float64) if want_rows else None
     y = np.empty((n_tok * k, H), np.float64) if want_rows else None
-    _check(_load().orc_moe_layer(M, H, F, E, k, S, expert_base, local_experts, dt, _p(x), _p(logits),
+    _check(_load().orc_moe_layer(M, H, F, E, k, S, expert_base, local_experts, dt, act_fp8, _p(x), _p(logits),
                                  _p(src_block), _p(wg), _p(wu), _p(wd), n_tok, _p(tok), _p(r["topk_idx"]),
                                  _p(r["topk_w"]), _p(r["counts"]), _p(r["offsets"]), _p(r["sorted_to_flat"]),
                                  _p(r["flat_to_sorted"]), _p(r["out"]), _p(hact), _p(y)), "moe_layer")

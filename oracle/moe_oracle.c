@@ -29,6 +29,13 @@
  *   combine  -> out[t] = sum_j w[t,j] * Y[flat_to_sorted[t*k+j]], summed from
  *               zero in slot order j = 0..k-1 (COMET review §4.1.1 Top-K
  *               reduction; PTO MoE article "Combine / Unpermute").
+ *   fp8 act  -> optionally the activation is quantised as SwiGLU produces it
+ *               (PTO MoE article, two-stage SwiGLU: each segment consumed
+ *               and quantised at once) and the down product runs on the
+ *               quantised values.  The format is the open OCP microscaling
+ *               one, MXFP8 with e4m3 elements: blocks of 32 values along F
+ *               share a power-of-two scale; W_down is given in the same
+ *               format (see the fp8 section below).
  *   epilogue -> out = cast(acc + residual) (grouped-GEMM article, fused
  *               GemmAdd epilogue: the accumulator plus an added tensor,
  *               then the cast to the output type), bf16 by round to
@@ -103,6 +110,95 @@ uint16_t orc_double_to_bf16_bits(double x) {
   uint32_t u;
   memcpy(&u, &f, sizeof u);
   return (uint16_t)(u >> 16);
+}
+
+/* -------------------------------------------------------------- MX fp8 --- */
+
+/*
+ * e4m3 ("fn" variant of the OCP 8-bit formats): sign, 4 exponent bits with
+ * bias 7, 3 mantissa bits; exponent field 0 holds the subnormals m/8 * 2^-6;
+ * the all-ones exponent is a normal binade except code 0x7F/0xFF, NaN.  The
+ * largest value is 1.75 * 2^8 = 448.
+ */
+double orc_e4m3_value(uint8_t code) {
+  int s = code >> 7, e = (code >> 3) & 15, m = code & 7;
+  if (e == 15 && m == 7) return NAN;
+  double v = (e == 0) ? ldexp((double)m, -9) : ldexp(8.0 + m, e - 10);
+  return s ? -v : v;
+}
+
+/* Nearest e4m3 code to v: every non-negative finite code is compared, a tie
+ * goes to the even code; magnitudes beyond 448 give 448 (the largest code
+ * compared); the sign bit is v's. */
+uint8_t orc_e4m3_round(double v) {
+  double a = fabs(v);
+  int best = 0;
+  double bd = INFINITY;
+  for (int c = 0; c < 127; ++c) {
+    double d = fabs(orc_e4m3_value((uint8_t)c) - a);
+    if (d < bd || (d == bd && (c & 1) == 0)) {
+      bd = d;
+      best = c;
+    }
+  }
+  return (uint8_t)(best | (signbit(v) ? 0x80 : 0));
+}
+
+/*
+ * MXFP8 block of 32 values (OCP microscaling formats): X = floor(log2 of the
+ * largest magnitude) - 8 (8 being the exponent of e4m3's largest value),
+ * kept within the scale's range [-127, 127], and -127 for an all-zero block;
+ * the scale byte is X + 127; each element is the e4m3 code nearest v / 2^X.
+ */
+static void mx_block(const double* v, uint8_t* codes, uint8_t* scale) {
+  double amax = 0.0;
+  for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs(v[i]));
+  int X = -127;
+  if (amax > 0.0) {
+    int e;
+    frexp(amax, &e); /* amax = m 2^e, 0.5 <= m < 1: floor(log2 amax) = e - 1 */
+    X = e - 1 - 8;
+    if (X < -127) X = -127;
+    if (X > 127) X = 127;
+  }
+  for (int i = 0; i < 32; ++i) codes[i] = orc_e4m3_round(ldexp(v[i], -X));
+  *scale = (uint8_t)(X + 127);
+}
+
+/* Value of element i of an MX row (codes, and one scale byte per 32). */
+static double mx_value(const uint8_t* codes, const uint8_t* scales, int64_t i) {
+  return ldexp(orc_e4m3_value(codes[i]), (int)scales[i / 32] - 127);
+}
+
+/*
+ * Quantise rows x cols values (cols a multiple of 32; f32 or bf16 bits, or
+ * doubles when dtype is -1) into one buffer: rows*cols codes, then
+ * rows*cols/32 scale bytes, row-major, the layout the down weights take.
+ */
+int orc_mx_quantize(int64_t rows, int cols, int dtype, const void* src, uint8_t* dst) {
+  if (rows < 0 || cols < 32 || cols % 32) return ORC_EINVAL;
+  uint8_t* scales = dst + rows * (int64_t)cols;
+  double blk[32];
+  for (int64_t r = 0; r < rows; ++r)
+    for (int b = 0; b < cols / 32; ++b) {
+      for (int i = 0; i < 32; ++i) {
+        int64_t idx = r * cols + b * 32 + i;
+        blk[i] = dtype < 0 ? ((const double*)src)[idx]
+                           : (dtype == ORC_F32 ? (double)((const float*)src)[idx]
+                                               : orc_bf16_bits_to_double(((const uint16_t*)src)[idx]));
+      }
+      mx_block(blk, dst + r * cols + b * 32, scales + r * (cols / 32) + b);
+    }
+  return ORC_OK;
+}
+
+/* Values of a quantised buffer (rows x cols) as doubles. */
+int orc_mx_dequantize(int64_t rows, int cols, const uint8_t* src, double* out) {
+  if (rows < 0 || cols < 32 || cols % 32) return ORC_EINVAL;
+  const uint8_t* scales = src + rows * (int64_t)cols;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int c = 0; c < cols; ++c) out[r * cols + c] = mx_value(src + r * cols, scales + r * (cols / 32), c);
+  return ORC_OK;
 }
 
 static double load_elem(const void* base, int dtype, int64_t i) {
@@ -231,9 +327,12 @@ static double silu(double z) { return z / (1.0 + exp(-z)); }
  * One routed row through expert e: Layer0 (gate and up products, SwiGLU,
  * bf16 rounding of the activation for bf16 layers), then Layer1 (down).
  * xrow is the token row widened to double.  hact [F] and y [H] in double.
+ * With act_fp8 the activation is instead quantised to MXFP8 in blocks of 32
+ * along F (hact holds the quantised values) and w_down is an MXFP8 buffer
+ * of E*H rows of F (codes, then scales).
  */
-static void ffn_row(int H, int F, int dtype, const double* xrow, const void* w_gate, const void* w_up,
-                    const void* w_down, int e, double* hact, double* y) {
+static void ffn_row(int H, int F, int dtype, int act_fp8, int E, const double* xrow, const void* w_gate,
+                    const void* w_up, const void* w_down, int e, double* hact, double* y) {
   int64_t eHF = (int64_t)e * H * F;
   for (int f = 0; f < F; ++f) {
     double g = 0.0, u = 0.0;
@@ -243,7 +342,25 @@ static void ffn_row(int H, int F, int dtype, const double* xrow, const void* w_g
       u += xrow[h] * load_elem(w_up, dtype, wrow + h);
     }
     double a = silu(g) * u;
-    hact[f] = (dtype == ORC_BF16) ? orc_round_to_bf16(a) : a;
+    /* the quantisation codes are decided on an f32 value, the precision the
+       activation has where it is quantised */
+    hact[f] = act_fp8 ? (double)(float)a : ((dtype == ORC_BF16) ? orc_round_to_bf16(a) : a);
+  }
+  if (act_fp8) {
+    uint8_t codes[32], sc;
+    for (int b = 0; b < F / 32; ++b) {
+      mx_block(hact + b * 32, codes, &sc);
+      for (int i = 0; i < 32; ++i) hact[b * 32 + i] = ldexp(orc_e4m3_value(codes[i]), (int)sc - 127);
+    }
+    const uint8_t* wc = (const uint8_t*)w_down;
+    const uint8_t* ws = wc + (int64_t)E * H * F;
+    for (int n = 0; n < H; ++n) {
+      double acc = 0.0;
+      int64_t wrow = eHF + (int64_t)n * F;
+      for (int f = 0; f < F; ++f) acc += hact[f] * mx_value(wc + wrow, ws + wrow / 32, f);
+      y[n] = acc;
+    }
+    return;
   }
   for (int n = 0; n < H; ++n) {
     double acc = 0.0;
@@ -266,10 +383,11 @@ static int64_t segment_of_row(const int32_t* offsets, int64_t G, int64_t r) {
  * input is X_perm[r] = x[sorted_to_flat[r] / k].
  * hact_out [n_rows, F] and y_out [n_rows, H] in double (either may be NULL).
  */
-int orc_ffn_rows(int H, int F, int E, int S, int k, int dtype, const void* x, const void* w_gate,
+int orc_ffn_rows(int H, int F, int E, int S, int k, int dtype, int act_fp8, const void* x, const void* w_gate,
                  const void* w_up, const void* w_down, const int32_t* sorted_to_flat, const int32_t* offsets,
                  int64_t n_rows, const int64_t* rows, double* hact_out, double* y_out) {
   if (H < 1 || F < 1 || E < 1 || S < 1 || k < 1 || (dtype != ORC_F32 && dtype != ORC_BF16)) return ORC_EINVAL;
+  if (act_fp8 && F % 32) return ORC_EINVAL;
   int64_t G = (int64_t)S * E;
   int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
@@ -283,7 +401,7 @@ int orc_ffn_rows(int H, int F, int E, int S, int k, int dtype, const void* x, co
     double* hact = (double*)malloc(sizeof(double) * (size_t)F);
     double* y = (double*)malloc(sizeof(double) * (size_t)H);
     for (int h = 0; h < H; ++h) xrow[h] = load_elem(x, dtype, t * H + h);
-    ffn_row(H, F, dtype, xrow, w_gate, w_up, w_down, e, hact, y);
+    ffn_row(H, F, dtype, act_fp8, E, xrow, w_gate, w_up, w_down, e, hact, y);
     if (hact_out) memcpy(hact_out + i * F, hact, sizeof(double) * (size_t)F);
     if (y_out) memcpy(y_out + i * H, y, sizeof(double) * (size_t)H);
     free(xrow); free(hact); free(y);
@@ -344,7 +462,8 @@ int orc_epilogue(int64_t n, const double* acc, const void* residual, int res_dty
  * hact [n_tok*k, F] and y [n_tok*k, H] double (may be NULL), row i*k+j
  * belongs to pair (tokens[i], j).
  */
-int orc_moe_layer(int64_t M, int H, int F, int E, int k, int S, int base, int EL, int dtype, const void* x,
+int orc_moe_layer(int64_t M, int H, int F, int E, int k, int S, int base, int EL, int dtype, int act_fp8,
+                  const void* x,
                   const float* logits, const int32_t* src_block, const void* w_gate, const void* w_up,
                   const void* w_down, int64_t n_tok, const int64_t* tokens, int32_t* topk_idx, float* topk_w,
                   int32_t* counts, int32_t* offsets, int32_t* sorted_to_flat, int32_t* flat_to_sorted, double* out,
@@ -379,8 +498,8 @@ int orc_moe_layer(int64_t M, int H, int F, int E, int k, int S, int base, int EL
   double* hk = (double*)malloc(sizeof(double) * (size_t)(n_kept > 0 ? n_kept : 1) * (size_t)F);
   double* yk = (double*)malloc(sizeof(double) * (size_t)(n_kept > 0 ? n_kept : 1) * (size_t)H);
   if (!rc)
-    rc = orc_ffn_rows(H, F, EL, S, k, dtype, x, w_gate, w_up, w_down, sorted_to_flat, offsets, n_kept, kept_rows,
-                      hk, yk);
+    rc = orc_ffn_rows(H, F, EL, S, k, dtype, act_fp8, x, w_gate, w_up, w_down, sorted_to_flat, offsets, n_kept,
+                      kept_rows, hk, yk);
   if (!rc) {
     int64_t q = 0;
     for (int64_t p = 0; p < n_pairs; ++p) {

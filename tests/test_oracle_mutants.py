@@ -23,7 +23,8 @@ MUTANTS = {
     "gate_up_swapped": ("double a = silu(g) * u;", "double a = silu(u) * g;"),
     "silu_sign": ("static double silu(double z) { return z / (1.0 + exp(-z)); }",
                   "static double silu(double z) { return z / (1.0 + exp(z)); }"),
-    "no_bf16_rounding": ("hact[f] = (dtype == ORC_BF16) ? orc_round_to_bf16(a) : a;", "hact[f] = a;"),
+    "no_bf16_rounding": ("hact[f] = act_fp8 ? (double)(float)a : ((dtype == ORC_BF16) ? orc_round_to_bf16(a) : a);",
+                         "hact[f] = act_fp8 ? (double)(float)a : a;"),
     "bf16_rounds_to_zero": ("double r = nearbyint(scaled);", "double r = trunc(scaled);"),
     "down_transposed": ("for (int f = 0; f < F; ++f) acc += hact[f] * load_elem(w_down, dtype, wrow + f);",
                         "for (int f = 0; f < F; ++f) acc += hact[f] * load_elem(w_down, dtype, eHF + (int64_t)f * H + n);"),
@@ -44,6 +45,14 @@ MUTANTS = {
     "epilogue_ignores_residual": ("double v = acc[i] + (residual ? load_elem(residual, res_dtype, i) : 0.0);",
                                   "double v = acc[i];"),
     "epilogue_not_rounded": ("out[i] = (out_dtype == ORC_BF16) ? orc_round_to_bf16(v) : v;", "out[i] = v;"),
+    "mx_scale_exponent_off_by_one": ("X = e - 1 - 8;", "X = e - 8;"),
+    "mx_ties_to_odd": ("if (d < bd || (d == bd && (c & 1) == 0)) {", "if (d < bd || (d == bd && (c & 1) == 1)) {"),
+    "mx_amax_skips_last": ("for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs(v[i]));",
+                           "for (int i = 0; i < 31; ++i) amax = fmax(amax, fabs(v[i]));"),
+    "mx_down_scale_index": ("acc += hact[f] * mx_value(wc + wrow, ws + wrow / 32, f);",
+                            "acc += hact[f] * mx_value(wc + wrow, ws + wrow, f);"),
+    "mx_act_not_quantised": ("for (int i = 0; i < 32; ++i) hact[b * 32 + i] = ldexp(orc_e4m3_value(codes[i]), (int)sc - 127);",
+                             ""),
     "epilogue_rounds_acc_first": ("double v = acc[i] + (residual ? load_elem(residual, res_dtype, i) : 0.0);",
                                   "double v = ((out_dtype == ORC_BF16) ? orc_round_to_bf16(acc[i]) : acc[i]) + "
                                   "(residual ? load_elem(residual, res_dtype, i) : 0.0);"),
@@ -78,6 +87,11 @@ def _checks():
         ("local_partition", pins.test_local_partition_sums_to_full_layer),
         ("epilogue_hand", pins.test_epilogue_hand_values),
         ("epilogue_torch", pins.test_epilogue_bf16_matches_torch_rounding_of_f32_sums),
+        ("e4m3_round", pins.test_e4m3_rounding_matches_torch_below_448),
+        ("e4m3_clamp", pins.test_e4m3_rounding_clamps_to_448),
+        ("mx_hand", pins.test_mx_block_hand_values),
+        ("mx_round_trip", pins.test_mx_round_trip_within_half_a_step),
+        ("mx_layer", pins.test_mx_layer_matches_dense_quantised_evaluation),
     ]
 
 

@@ -387,3 +387,94 @@ def test_layer_epilogue_is_applied_to_the_combined_output():
     want = torch.from_numpy((plain["out"] + widen(res)[toks]).astype(np.float32)).to(torch.bfloat16).double()
     # the f32 rounding of the sum is within half an f32 ulp: the bf16 results agree except at exact ties
     assert np.mean(r["out"] == want.numpy()) > 0.999
+
+
+# ----------------------------------------------------------- MXFP8 (NEXT) --
+# The activation quantised as SwiGLU produces it (PTO MoE article, two-stage
+# SwiGLU) in the open OCP microscaling format MXFP8: e4m3 elements, one
+# power-of-two scale per 32 values.
+
+def test_e4m3_decode_matches_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).double().numpy()
+    got = np.array([oracle.e4m3_value(c) for c in codes])
+    nan = (codes & 0x7F) == 0x7F
+    assert np.all(np.isnan(got[nan])) and np.array_equal(got[~nan], want[~nan])
+
+
+def test_e4m3_rounding_matches_torch_below_448():
+    rng = np.random.default_rng(101)
+    vals = np.concatenate([rng.standard_normal(4000) * 40, rng.standard_normal(2000) * 0.01,
+                           rng.uniform(-448, 448, 2000)])
+    # every midpoint between neighbouring codes (exact ties) and the codes themselves
+    pos = np.array([oracle.e4m3_value(c) for c in range(127)])
+    mids = (pos[:-1] + pos[1:]) / 2
+    vals = np.concatenate([vals, mids, -mids, pos, -pos]).astype(np.float32)
+    want = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.e4m3_round(float(v)) for v in vals], np.uint8)
+    assert np.array_equal(got, want)
+
+
+def test_e4m3_rounding_clamps_to_448():
+    for v, c in [(448.0, 0x7E), (449.0, 0x7E), (464.0, 0x7E), (480.0, 0x7E), (1e9, 0x7E), (-500.0, 0xFE),
+                 (0.0, 0x00), (2.0 ** -10, 0x00), (3 * 2.0 ** -10, 0x02)]:
+        assert oracle.e4m3_round(v) == c, (v, c)
+
+
+def test_mx_block_hand_values():
+    def q(block):
+        buf = oracle.mx_quantize(np.asarray(block, np.float64).reshape(1, 32))
+        return buf[:32], int(buf[32])
+    codes, s = q([1.0] * 32)            # floor(log2 1) - 8 = -8: 1 / 2^-8 = 256 = code 0x78
+    assert s == 127 - 8 and np.all(codes == 0x78)
+    codes, s = q([448.0] + [0.0] * 31)  # X = 0, 448 exact
+    assert s == 127 and codes[0] == 0x7E and np.all(codes[1:] == 0)
+    codes, s = q([500.0, -1.0] + [0.0] * 30)  # X = 0 (floor log2 500 = 8): 500 clamps to 448
+    assert s == 127 and codes[0] == 0x7E and codes[1] == 0xB8
+    codes, s = q([0.0] * 32)            # all zero: the smallest scale, zero codes
+    assert s == 0 and np.all(codes == 0)
+    codes, s = q([0.75] + [0.1] * 31)   # X = -1 - 8: 0.75 * 512 = 384 = 1.5 * 2^8 = 0x7C
+    assert s == 127 - 9 and codes[0] == 0x7C
+    assert abs(oracle.e4m3_value(codes[1]) * 2.0 ** -9 - 0.1) <= 0.1 * 2.0 ** -4
+
+
+def test_mx_round_trip_within_half_a_step():
+    rng = np.random.default_rng(103)
+    v = rng.standard_normal((64, 256)) * np.exp(rng.uniform(-8, 8, (64, 1)))
+    buf = oracle.mx_quantize(v)
+    d = oracle.mx_dequantize(buf, 64, 256)
+    scales = buf[64 * 256:].astype(np.int64).reshape(64, 8)
+    X = np.repeat(scales - 127, 32, axis=1)
+    t = np.abs(v) / 2.0 ** X                      # magnitude in units of the block scale
+    assert np.all(t.reshape(64, 8, 32).max(axis=2) >= 256) and np.all(t < 512)
+    half = np.where(t >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(t, 2.0 ** -6))) - 4), 2.0 ** -10)
+    err = np.abs(d - v) / 2.0 ** X
+    clamped = t > 448
+    assert np.all(err[~clamped] <= half[~clamped] * (1 + 1e-12))
+    assert np.all(np.abs(d[clamped]) == 448 * 2.0 ** X[clamped])
+    # values already on the grid come back exactly
+    assert np.array_equal(oracle.mx_dequantize(oracle.mx_quantize(d), 64, 256), d)
+
+
+def test_mx_layer_matches_dense_quantised_evaluation():
+    """The fp8-activation layer against a dense evaluation: every expert on
+    every token in numpy, the activation rounded to f32 and quantised by
+    blocks of 32 along F, the down product on the dequantised values."""
+    cfg, d = small_inputs(40, 64, 128, 4, 2, "bf16", 111)
+    wd_mx = oracle.mx_quantize(d["w_down"].reshape(4 * 64, 128))
+    r = oracle.moe_layer(d["x"], d["logits"], d["w_gate"], d["w_up"], d["w_down"], 2, w_down_mx=wd_mx)
+    X, L = widen(d["x"]), d["logits"].astype(np.float64)
+    Wg, Wu = widen(d["w_gate"]), widen(d["w_up"])
+    Wd = oracle.mx_dequantize(wd_mx, 4 * 64, 128).reshape(4, 64, 128)
+    order = np.argsort(-L, axis=1, kind="stable")[:, :2]
+    p = np.exp(L - L.max(axis=1, keepdims=True))
+    p = p / p.sum(axis=1, keepdims=True)
+    out = np.zeros((40, 64))
+    for e in range(4):
+        G, U = X @ Wg[e].T, X @ Wu[e].T
+        h = (G / (1.0 + np.exp(-G)) * U).astype(np.float32).astype(np.float64)
+        hq = oracle.mx_dequantize(oracle.mx_quantize(h), 40, 128)
+        mask = (order == e).any(axis=1)
+        w = np.where(mask, p[:, e] / np.take_along_axis(p, order, axis=1).sum(axis=1), 0.0)
+        out += w.astype(np.float32).astype(np.float64)[:, None] * (hq @ Wd[e].T)
+    np.testing.assert_allclose(r["out"], out, rtol=1e-9, atol=1e-12)

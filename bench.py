@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 PEAK_F32_TFLOPS = 157.3     # MI355X f32 matrix peak
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 matrix-core peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
@@ -45,6 +46,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--n-mover", type=int, default=-1)
+    ap.add_argument("--act", choices=("bf16", "mxfp8"), default="bf16",
+                    help="mxfp8: Hact and W_down in MXFP8 (W_down quantised on the GPU before timing)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (to scale the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
@@ -157,12 +160,21 @@ def main():
 
     moe.load_library()
     cfg = moe_synth.config(args.config)
+    if args.act == "mxfp8":
+        cfg = moe_synth.config(args.config, dtype="bf16_mxfp8")
     d = moe_synth.make_inputs(cfg)
     g = upload(d)
+    mx = cfg.dtype == "bf16_mxfp8"
+    w_down = g["w_down"]
+    if mx:
+        # the layer's input format: W_down in MXFP8, quantised once before timing
+        w_down = torch.empty(moe.mx_bytes(cfg.EL * cfg.H, cfg.F), dtype=torch.uint8, device="cuda:0")
+        moe.moe_quantize_mxfp8(g["w_down"], w_down)
+        torch.cuda.synchronize()
     dev = torch.device("cuda:0")
     p = moe.problem(cfg.M, cfg.H, cfg.F, cfg.E, cfg.k, cfg.S, cfg.dtype, cfg.base, cfg.local)
     M, k, H, F, G, R = cfg.M, cfg.k, cfg.H, cfg.F, cfg.S * cfg.EL, cfg.R
-    act = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    act = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
     idx = torch.empty((M, k), dtype=torch.int32, device=dev)
     w = torch.empty((M, k), dtype=torch.float32, device=dev)
     counts = torch.empty(G, dtype=torch.int32, device=dev)
@@ -170,7 +182,8 @@ def main():
     s2f = torch.empty(R, dtype=torch.int32, device=dev)
     f2s = torch.empty(R, dtype=torch.int32, device=dev)
     xp = torch.empty((R, H), dtype=act, device=dev)
-    hact = torch.empty((R, F), dtype=act, device=dev)
+    hact = torch.empty(moe.mx_bytes(R, F), dtype=torch.uint8, device=dev) if mx else \
+        torch.empty((R, F), dtype=act, device=dev)
     y = torch.empty((R, H), dtype=torch.float32, device=dev)
     out = torch.empty((M, H), dtype=torch.float32, device=dev)
     ws_d = torch.empty(max(4, moe.moe_workspace_bytes(p, moe.MOE_OP_DISPATCH)), dtype=torch.uint8, device=dev)
@@ -204,14 +217,14 @@ def main():
         if ev: ev[2].record(stream)
         moe.moe_grouped_gemm(p, 0, xp, g["w_gate"], g["w_up"], offsets, hact, ws_g, stream)
         if ev: ev[3].record(stream)
-        moe.moe_grouped_gemm(p, 1, hact, g["w_down"], None, offsets, y, ws_g, stream)
+        moe.moe_grouped_gemm(p, 1, hact, w_down, None, offsets, y, ws_g, stream)
         if ev: ev[4].record(stream)
         moe.moe_combine(p, y, w, f2s, out, stream)
         if ev: ev[5].record(stream)
 
     def step_layer(ev):
         if ev: ev[0].record(stream)
-        moe.moe_layer(p, g["x"], g["logits"], src, g["w_gate"], g["w_up"], g["w_down"], out, ws_l,
+        moe.moe_layer(p, g["x"], g["logits"], src, g["w_gate"], g["w_up"], w_down, out, ws_l,
                       n_mover=args.n_mover, fused=0 if args.mode == "chain" else 1, stream=stream)
         if ev: ev[1].record(stream)
 
@@ -243,10 +256,11 @@ def main():
     res = {"metric": "MoE layer us + grouped-GEMM TFLOP/s (% MFMA peak), Mixtral shape M=8192",
            "value": flops / (ms_step * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+           "vs_baseline": None, "dtype": {"bf16": "bf16", "f32": "f32", "bf16_mxfp8": "bf16+mxfp8"}[cfg.dtype],
            "data": "synthetic (seeded N(0,1) tokens and logits, N(0,0.02^2) weights, random-init)",
            "config": {"workload": f"{cfg.name}: MoE layer M={M} H={H} F={F} E={cfg.E} topk={k} S={cfg.S}"
-                      + (f" experts held {cfg.base}..{cfg.base + cfg.EL - 1}" if cfg.local else ""),
+                      + (f" experts held {cfg.base}..{cfg.base + cfg.EL - 1}" if cfg.local else "")
+                      + (", Hact and W_down MXFP8" if mx else ""),
                       "tokens": M, "hidden": H, "ffn": F, "experts": cfg.E, "topk": k, "src_blocks": cfg.S,
                       "experts_held": cfg.EL, "routed_rows_held": Rk,
                       "layer_call": "fused" if (args.mode == "layer" and movers >= 0 and cfg.dtype == "bf16")
@@ -256,9 +270,15 @@ def main():
     names = ["route", "dispatch", "gemm_l0", "gemm_l1", "combine"]
     res["step_us"] = {n: float(v) for n, v in zip(names, mean)}
     t_gemm = (mean[2] + mean[3]) * 1e-6
-    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    peak = PEAK_F32_TFLOPS if cfg.dtype == "f32" else PEAK_BF16_TFLOPS
     res["grouped_gemm_tflops"] = flops / t_gemm / 1e12
-    res["grouped_gemm_pct_peak"] = 100.0 * res["grouped_gemm_tflops"] / peak
+    if mx:
+        # Layer0 at the bf16 peak, Layer1 (MXFP8) at the fp8 peak
+        ideal = (4.0 * Rk * H * F / PEAK_BF16_TFLOPS + 2.0 * Rk * H * F / PEAK_FP8_TFLOPS) / 1e12
+        res["grouped_gemm_pct_peak"] = 100.0 * ideal / t_gemm
+        res["gemm_l1_mxfp8_pct_peak"] = 100.0 * 2.0 * Rk * H * F / (mean[3] * 1e-6) / 1e12 / PEAK_FP8_TFLOPS
+    else:
+        res["grouped_gemm_pct_peak"] = 100.0 * res["grouped_gemm_tflops"] / peak
     eb = 2 if cfg.dtype == "bf16" else 4
     # token rows read (those with a held pair), rows written, the index list
     disp_bytes = Tk * H * eb + Rk * H * eb + R * 4

@@ -30,14 +30,15 @@ MOE_ERR_DEVICE_TIMEOUT = 5
 
 MOE_DTYPE_F32 = 0
 MOE_DTYPE_BF16 = 1
+MOE_DTYPE_BF16_MXFP8 = 2
 
 MOE_OP_DISPATCH = 0
 MOE_OP_GROUPED_GEMM = 1
 MOE_OP_LAYER = 2
 
 EXPORTED = ("moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_grouped_gemm", "moe_combine", "moe_combine_ex",
-            "moe_layer", "moe_layer_ex", "moe_layer_default_movers", "moe_debug_device_status", "moe_status_string",
-            "moe_abi_version")
+            "moe_layer", "moe_layer_ex", "moe_quantize_mxfp8", "moe_layer_default_movers", "moe_debug_device_status",
+            "moe_status_string", "moe_abi_version")
 
 
 class MoeError(RuntimeError):
@@ -90,6 +91,7 @@ def load_library(path: str = LIB_PATH):
         "moe_layer": ([PP, P, P, P, P, P, P, P, ctypes.POINTER(LayerAux), ctypes.POINTER(LayerOpts), P, SZ, P], I32),
         "moe_layer_ex": ([PP, P, P, P, P, P, P, ctypes.POINTER(Epilogue), P, ctypes.POINTER(LayerAux),
                           ctypes.POINTER(LayerOpts), P, SZ, P], I32),
+        "moe_quantize_mxfp8": ([ctypes.c_int64, I32, I32, P, P, P], I32),
         "moe_layer_default_movers": ([PP], I32),
         "moe_debug_device_status": ([PP, P, SZ, P], I32),
         "moe_status_string": ([I32], ctypes.c_char_p),
@@ -110,7 +112,13 @@ def status_name(status: int) -> str:
         return str(status)
 
 
-_DTYPES = {"bf16": MOE_DTYPE_BF16, "f32": MOE_DTYPE_F32, MOE_DTYPE_BF16: MOE_DTYPE_BF16, MOE_DTYPE_F32: MOE_DTYPE_F32}
+_DTYPES = {"bf16": MOE_DTYPE_BF16, "f32": MOE_DTYPE_F32, "bf16_mxfp8": MOE_DTYPE_BF16_MXFP8,
+           MOE_DTYPE_BF16: MOE_DTYPE_BF16, MOE_DTYPE_F32: MOE_DTYPE_F32, MOE_DTYPE_BF16_MXFP8: MOE_DTYPE_BF16_MXFP8}
+
+
+def mx_bytes(rows: int, cols: int) -> int:
+    """Bytes of an MXFP8 buffer of rows x cols (codes, then one scale per 32)."""
+    return rows * cols + rows * cols // 32
 
 
 def problem(M, H, F, E, k, S=1, dtype="bf16", expert_base=0, local_experts=0) -> Problem:
@@ -187,6 +195,17 @@ def moe_combine_ex(p, y, topk_w, flat_to_sorted, epi, out, stream=None):
     _check(load_library().moe_combine_ex(ctypes.byref(p), _ptr(y), _ptr(topk_w), _ptr(flat_to_sorted),
                                          ctypes.byref(epi) if epi is not None else None, _ptr(out),
                                          _stream(stream)), "moe_combine_ex")
+
+
+def moe_quantize_mxfp8(src, dst, stream=None):
+    """MXFP8 quantisation of a 2-D (or stacked) bf16/f32 tensor along its last
+    dimension into dst (uint8, mx_bytes(rows, cols) bytes)."""
+    import torch
+    cols = src.shape[-1]
+    rows = src.numel() // cols
+    dt = MOE_DTYPE_BF16 if src.dtype == torch.bfloat16 else MOE_DTYPE_F32
+    _check(load_library().moe_quantize_mxfp8(rows, cols, dt, _ptr(src), _ptr(dst), _stream(stream)),
+           "moe_quantize_mxfp8")
 
 
 def moe_layer(p, x, logits, src_block, w_gate, w_up, w_down, out, ws, aux: dict | None = None,

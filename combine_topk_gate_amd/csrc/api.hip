@@ -17,7 +17,13 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-size_t elem_bytes(const moe_problem_t* p) { return p->dtype == MOE_DTYPE_BF16 ? 2 : 4; }
+// bytes per element of x and X_perm (and of Hact unless it is MXFP8)
+size_t elem_bytes(const moe_problem_t* p) { return p->dtype == MOE_DTYPE_F32 ? 4 : 2; }
+bool is_mx(const moe_problem_t* p) { return p->dtype == MOE_DTYPE_BF16_MXFP8; }
+// bytes of the Hact buffer: R x F elements, or an MXFP8 buffer (codes + scales)
+size_t hact_bytes(const moe_problem_t* p, int64_t R) {
+  return is_mx(p) ? (size_t)R * p->ffn + (size_t)R * (p->ffn / 32) : (size_t)R * p->ffn * elem_bytes(p);
+}
 
 // Experts held by the call (weights it is given): EL, or all E.
 int held(const moe_problem_t* p) { return p->local_experts > 0 ? p->local_experts : p->num_experts; }
@@ -39,7 +45,9 @@ moe_status_t check_problem(const moe_problem_t* p) {
   // dropped pairs take one more segment in the bookkeeping
   const int64_t ranked = (int64_t)p->num_src_blocks * held(p) + (held(p) < p->num_experts ? 1 : 0);
   if (p->num_src_blocks < 1 || ranked > 1024) return MOE_ERR_INVALID_ARGUMENT;
-  if (p->dtype != MOE_DTYPE_F32 && p->dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARGUMENT;
+  if (p->dtype != MOE_DTYPE_F32 && p->dtype != MOE_DTYPE_BF16 && p->dtype != MOE_DTYPE_BF16_MXFP8)
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (p->dtype == MOE_DTYPE_BF16_MXFP8 && p->ffn % 128) return MOE_ERR_UNSUPPORTED;
   const int64_t R = M * p->topk;
   if (R >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
   const int64_t wide = p->hidden > p->ffn ? p->hidden : p->ffn;
@@ -56,7 +64,7 @@ PermutePlan plan_of(const moe_problem_t* p) {
 moe_status_t epilogue_of(const moe_problem_t* p, const moe_epilogue_t* epi, void* out, OutEpilogue* ep) {
   ep->out = out;
   ep->residual = nullptr;
-  ep->res_bf16 = p->dtype == MOE_DTYPE_BF16;
+  ep->res_bf16 = p->dtype != MOE_DTYPE_F32;  // the dtype of x: bf16 for the bf16 and MXFP8 layers
   ep->out_bf16 = 0;
   if (epi) {
     if (epi->out_dtype != MOE_DTYPE_F32 && epi->out_dtype != MOE_DTYPE_BF16) return MOE_ERR_INVALID_ARGUMENT;
@@ -91,11 +99,11 @@ LayerWs layer_ws(const moe_problem_t* p) {
   w.f2s = o; o += align_up((size_t)R * 4);
   w.perm = o; o += align_up(permute_ws_bytes(pl));
   w.x_perm = o; o += align_up((size_t)R * p->hidden * eb);
-  w.hact = o; o += align_up((size_t)R * p->ffn * eb);
+  w.hact = o; o += align_up(hact_bytes(p, R));
   w.y = o; o += align_up((size_t)R * p->hidden * 4);
   w.fused = o; o += align_up(fused_ws_bytes(p->num_tokens, p->hidden, p->ffn, held(p), p->topk,
                                              p->num_src_blocks));
-  w.gemm = o; o += align_up(p->dtype == MOE_DTYPE_BF16 ? gemm_split_ws_bytes() : 0);
+  w.gemm = o; o += align_up(p->dtype == MOE_DTYPE_BF16 ? gemm_split_ws_bytes() : 0);  // MXFP8 does not split
   w.total = o;
   return w;
 }
@@ -193,6 +201,7 @@ moe_status_t moe_grouped_gemm(const moe_problem_t* p, int32_t layer, const void*
   gp.ws = ws;
   gp.ws_bytes = ws ? ws_bytes : 0;
   hipStream_t s = (hipStream_t)stream;
+  if (is_mx(p)) return hip_status(launch_grouped_gemm_mx(gp, s));
   return hip_status(p->dtype == MOE_DTYPE_BF16 ? launch_grouped_gemm_bf16(gp, s) : launch_grouped_gemm_f32(gp, s));
 }
 
@@ -339,7 +348,8 @@ moe_status_t moe_layer_ex(const moe_problem_t* p, const void* x, const float* lo
   gp.N = p->ffn;
   gp.ws = at<void>(ws, L.gemm);
   gp.ws_bytes = L.total - L.gemm;
-  e = p->dtype == MOE_DTYPE_BF16 ? launch_grouped_gemm_bf16(gp, s) : launch_grouped_gemm_f32(gp, s);
+  e = is_mx(p) ? launch_grouped_gemm_mx(gp, s)
+              : (p->dtype == MOE_DTYPE_BF16 ? launch_grouped_gemm_bf16(gp, s) : launch_grouped_gemm_f32(gp, s));
   if (e != hipSuccess) return MOE_ERR_HIP;
   gp.layer = 1;
   gp.a = hact;
@@ -348,7 +358,8 @@ moe_status_t moe_layer_ex(const moe_problem_t* p, const void* x, const float* lo
   gp.c = y;
   gp.K = p->ffn;
   gp.N = p->hidden;
-  e = p->dtype == MOE_DTYPE_BF16 ? launch_grouped_gemm_bf16(gp, s) : launch_grouped_gemm_f32(gp, s);
+  e = is_mx(p) ? launch_grouped_gemm_mx(gp, s)
+              : (p->dtype == MOE_DTYPE_BF16 ? launch_grouped_gemm_bf16(gp, s) : launch_grouped_gemm_f32(gp, s));
   if (e != hipSuccess) return MOE_ERR_HIP;
   return hip_status(launch_combine(y, w, f2s, M, p->hidden, p->topk, ep, s));
 }
@@ -358,6 +369,16 @@ moe_status_t moe_layer(const moe_problem_t* p, const void* x, const float* logit
                        const moe_layer_aux_t* aux, const moe_layer_opts_t* opts, void* ws, size_t ws_bytes,
                        void* stream) {
   return moe_layer_ex(p, x, logits, src_block, w_gate, w_up, w_down, nullptr, out, aux, opts, ws, ws_bytes, stream);
+}
+
+moe_status_t moe_quantize_mxfp8(int64_t rows, int32_t cols, int32_t src_dtype, const void* src, void* dst,
+                                void* stream) {
+  if (rows < 0 || cols < 32 || cols % 32) return MOE_ERR_INVALID_ARGUMENT;
+  if (src_dtype != MOE_DTYPE_BF16 && src_dtype != MOE_DTYPE_F32) return MOE_ERR_INVALID_ARGUMENT;
+  if (rows == 0) return MOE_OK;
+  if (!src || !dst || !aligned(src, 16) || !aligned(dst, 16)) return MOE_ERR_INVALID_ARGUMENT;
+  if (rows * (int64_t)cols >= (1ll << 40)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(launch_mx_quantize(src, src_dtype == MOE_DTYPE_BF16, rows, cols, dst, (hipStream_t)stream));
 }
 
 moe_status_t moe_debug_device_status(const moe_problem_t* p, void* ws, size_t ws_bytes, void* stream) {

@@ -43,6 +43,36 @@ __device__ __forceinline__ float silu_mul_fast(float g, float u) {
   return (g * u) * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// MXFP8 (the OCP microscaling format with e4m3 elements): a block of 32
+// values shares the scale 2^X, X = floor(log2 of the block's largest
+// magnitude) - 8 (8 is the exponent of e4m3's largest value, 448), within
+// [-127, 127]; -127 for an all-zero block.  The scale byte is X + 127.
+__device__ __forceinline__ int mx_scale(float amax) {
+  const int ef = (int)((__builtin_bit_cast(uint32_t, amax) >> 23) & 0xFF);
+  if (ef == 0) return -127;  // zero, or below the smallest normal f32
+  const int X = ef - 127 - 8;
+  return X < -127 ? -127 : X;
+}
+
+// e4m3 code of v (already divided by the block scale, |v| < 512): round to
+// nearest, ties to even, magnitudes past 448 give 448 (0x7E); sign of v.
+// Normal range (|v| >= 2^-6): v = 2^E (1 + m/8), code (E + 7) * 8 + m, where
+// a mantissa rounded up to 8 carries into the exponent by itself;
+// subnormals are multiples of 2^-9 (code = the multiple, 8 = 2^-6).
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  const uint32_t bits = __builtin_bit_cast(uint32_t, v);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const float a = __builtin_bit_cast(float, bits & 0x7FFFFFFFu);
+  int code;
+  if (a >= 0x1p-6f) {
+    const int E = (int)((bits >> 23) & 0xFF) - 127;
+    code = (E + 7) * 8 + (int)rintf((ldexpf(a, -E) - 1.0f) * 8.0f);
+  } else {
+    code = (int)rintf(a * 512.0f);
+  }
+  return sign | (uint32_t)(code < 126 ? code : 126);
+}
+
 // Top-k weighted reduction of one 4-wide column group, shared by the
 // stand-alone combine and the fused layer so both give identical bits.
 // A slot whose row is -1 (a pair of an expert not held here) is left out.

@@ -53,7 +53,13 @@ struct Bf16GemmArgs {
   const __bf16* a;   // token rows [R, K]; gather mode: token-major x [M, K]
   const __bf16* w0;  // layer 0: W_gate [E, F, H]; layer 1: W_down [E, H, F]
   const __bf16* w1;  // layer 0: W_up [E, F, H]
-  void* c;           // layer 0: Hact [R, F] bf16; layer 1: Y [R, H] f32
+  void* c;           // layer 0: Hact [R, F] bf16 (or MXFP8 codes); layer 1: Y [R, H] f32
+  // MXFP8 (one e8m0 scale byte per 32 values along the reduction index):
+  // layer 0 writes Hact's scales [R, F/32] here; layer 1 reads the token
+  // rows' and the weights' scales ([R, F/32] and [E, H, F/32])
+  uint8_t* c_scale;
+  const uint8_t* a_scale;
+  const uint8_t* w_scale;
   int K, N, E;
   // gather mode (layer 0 inside the fused layer): sorted row r reads token
   // row sorted_to_flat[r] / topk of x directly, so X_perm is never written
@@ -76,12 +82,16 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 // accumulators of the tile to part[t * 256 + w] (t = tile token row < trows,
 // w = the tile's weight row); the caller adds the K ranges of a tile in a
 // fixed order.  Otherwise k0 = 0, k1 = K / kBK (the whole reduction).
-template <int LAYER, bool GATHER = false, int TM = kTileRows, bool PARTIAL = false>
+//
+// OUT8 (layer 0): Hact is written as MXFP8 instead of bf16: e4m3 codes and,
+// per 32 columns of a token row, one scale byte (see mx_scale / e4m3_code).
+template <int LAYER, bool GATHER = false, int TM = kTileRows, bool PARTIAL = false, bool OUT8 = false>
 __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int seg_start, int seg_rows, int m0,
                                                int nt, char* __restrict__ lds, int k0 = 0, int k1 = -1,
                                                float* __restrict__ part = nullptr) {
   static_assert(TM == 256 || TM == 128, "token tile height");
   static_assert(!PARTIAL || (TM == 256 && LAYER == 1), "partial tiles: layer 1, full height");
+  static_assert(!OUT8 || (LAYER == 0 && !PARTIAL), "MXFP8 output: layer 0");
   constexpr int NJ = TM / 64;      // token fragments per wave
   constexpr int XI = TM / 32;      // token-row loads per thread per K step
   constexpr int XQ = XI / 4;       // ... per sub-step
@@ -406,6 +416,59 @@ __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int
       }
       __syncthreads();
     }
+  } else if (LAYER == 0 && OUT8) {
+    // MXFP8: h (f32) is staged as 512 B per row (128 columns; 16-byte unit
+    // u of row t at u ^ (t & 31)), then each thread quantises one block of
+    // 32 columns of a row: the block's largest magnitude, its scale, 32
+    // codes.  Four threads cover a row, so the 128 code bytes of a row are
+    // stored contiguously.
+    char* stg = lds;
+#pragma unroll
+    for (int nj = 0; nj < NJ; ++nj) {
+      const int t = wm * (TM / 2) + nj * 32 + lrow;
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          f32x4_t h;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) h[v] = silu_mul_fast(acc[mi][nj][4 * q + v], acc[mi + 2][nj][4 * q + v]);
+          const int u = wn * 16 + mi * 8 + 2 * q + lk;
+          *reinterpret_cast<f32x4_t*>(stg + t * 512 + ((u ^ (t & 31)) << 4)) = h;
+        }
+      }
+    }
+    __syncthreads();
+    uint8_t* hact = reinterpret_cast<uint8_t*>(p.c);
+    const int b = tid & 3;
+    const int f = col0 + 32 * b;
+    for (int t = tid >> 2; t < TM; t += kGemmThreads / 4) {
+      f32x4_t v[8];
+      float amax = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        v[j] = *reinterpret_cast<const f32x4_t*>(stg + t * 512 + (((8 * b + j) ^ (t & 31)) << 4));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(v[j][i]));
+      }
+      const int X = mx_scale(amax);
+      i32x4_t out[2];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w |= e4m3_code(ldexpf(v[j][i], -X)) << (8 * i);
+        out[j / 4][j % 4] = (int)w;
+      }
+      const int trow = m0 + t;
+      if (trow < seg_rows && f < N) {
+        uint8_t* dst = hact + (int64_t)(seg_start + trow) * N + f;
+        *reinterpret_cast<i32x4_t*>(dst) = out[0];
+        *reinterpret_cast<i32x4_t*>(dst + 16) = out[1];
+        p.c_scale[(int64_t)(seg_start + trow) * (N / 32) + f / 32] = (uint8_t)(X + 127);
+      }
+    }
+    __syncthreads();
   } else if (LAYER == 0) {
     // 256 B per staged row (128 bf16 columns); 8-byte unit u of row t at
     // unit u ^ (t & 31): conflict-free for 32 rows writing the same unit.
@@ -491,13 +554,13 @@ __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int
 // running at once on an XCD stay in step and share the segment's weight
 // panels in its L2 (measured: halving those last tiles cost more in
 // re-read weights than it saved).
-template <int LAYER, bool GATHER = false>
+template <int LAYER, bool GATHER = false, bool OUT8 = false>
 __device__ __forceinline__ void bf16_gemm_row_tile(const Bf16GemmArgs& p, int g, int seg_start, int seg_rows, int m0,
                                                    int nt, char* __restrict__ lds) {
   if (seg_rows <= kTileRows / 2)
-    bf16_gemm_tile<LAYER, GATHER, kTileRows / 2>(p, g, seg_start, seg_rows, m0, nt, lds);
+    bf16_gemm_tile<LAYER, GATHER, kTileRows / 2, false, OUT8>(p, g, seg_start, seg_rows, m0, nt, lds);
   else
-    bf16_gemm_tile<LAYER, GATHER>(p, g, seg_start, seg_rows, m0, nt, lds);
+    bf16_gemm_tile<LAYER, GATHER, kTileRows, false, OUT8>(p, g, seg_start, seg_rows, m0, nt, lds);
 }
 
 }  // namespace moe

@@ -8,6 +8,7 @@
 // pure function of the offsets.
 #include "common.hpp"
 #include "gemm_bf16.hpp"
+#include "gemm_mx.hpp"
 #include "launch.hpp"
 #include "tiles.hpp"
 
@@ -51,7 +52,9 @@ __device__ __forceinline__ bool split_pays(int nk, int s, bool halfable) {
 //    element exactly as a full tile does.
 // The split is a function of the tile count and the grid, so a given device
 // always splits the same tiles the same way.
-template <int LAYER>
+// OUT8 (layer 0): Hact is written in MXFP8 (codes to args.c, scales to
+// args.c_scale) for the MXFP8 Layer1 below.
+template <int LAYER, bool OUT8 = false>
 __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(Bf16GemmArgs args,
                                                                          const int32_t* __restrict__ offsets, int G,
                                                                          int group_cols, SplitWs split) {
@@ -61,7 +64,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(Bf16Gem
   const int T = build_tile_table(offsets, G, kTileRows, tl) * NT;
   const int grid = gridDim.x;
   const int r = T % grid;
-  if constexpr (LAYER == 1) {
+  if constexpr (LAYER == 1 && !OUT8) {
     const int nk = args.K / kBK;
     int s = 1;
     if (split.hdr && r > 0) s = min(min(grid / r, nk / kMinSplitSteps), kMaxSplit);
@@ -100,14 +103,89 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(Bf16Gem
   for (int v = xcd_slot(blockIdx.x, grid); v < entries; v += grid) {
     if (v < T - half) {
       const TileCoord c = tile_coord(v, G, NT, kTileRows, group_cols, tl);
-      bf16_gemm_row_tile<LAYER>(args, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], c.m0, c.nt, lds);
+      bf16_gemm_row_tile<LAYER, false, OUT8>(args, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], c.m0, c.nt, lds);
     } else {
       const int j = v - (T - half);
       const TileCoord c = tile_coord(T - half + j / 2, G, NT, kTileRows, group_cols, tl);
       const int m0 = c.m0 + (j & 1) * (kTileRows / 2);
-      if (m0 < tl.seg_rows[c.g]) bf16_gemm_tile<LAYER, false, kTileRows / 2>(args, c.g, tl.seg_start[c.g],
-                                                                              tl.seg_rows[c.g], m0, c.nt, lds);
+      if (m0 < tl.seg_rows[c.g])
+        bf16_gemm_tile<LAYER, false, kTileRows / 2, false, OUT8>(args, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], m0,
+                                                                 c.nt, lds);
     }
+  }
+}
+
+// Layer1 on MXFP8 operands: the same persistent schedule (tile order,
+// half-height tiles for single-tile segments of at most 128 rows and for a
+// last round that would leave more than half the CUs idle) with the MXFP8
+// tile; no split of the last round.
+__global__ __launch_bounds__(kGemmThreads) void grouped_gemm_mx_kernel(Bf16GemmArgs args,
+                                                                       const int32_t* __restrict__ offsets, int G,
+                                                                       int group_cols) {
+  __shared__ __attribute__((aligned(16))) char lds[kGemmLdsBytes];
+  __shared__ TileLds tl;
+  const int NT = (args.N + kL1Cols - 1) / kL1Cols;
+  const int T = build_tile_table(offsets, G, kTileRows, tl) * NT;
+  const int grid = gridDim.x;
+  const int r = T % grid;
+  const int half = (r > 0 && 2 * r <= grid && T > grid) ? r : 0;
+  const int entries = T + half;
+  for (int v = xcd_slot(blockIdx.x, grid); v < entries; v += grid) {
+    if (v < T - half) {
+      const TileCoord c = tile_coord(v, G, NT, kTileRows, group_cols, tl);
+      if (tl.seg_rows[c.g] <= kTileRows / 2)
+        mx_gemm_tile<kTileRows / 2>(args, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], c.m0, c.nt, lds);
+      else
+        mx_gemm_tile<kTileRows>(args, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], c.m0, c.nt, lds);
+    } else {
+      const int j = v - (T - half);
+      const TileCoord c = tile_coord(T - half + j / 2, G, NT, kTileRows, group_cols, tl);
+      const int m0 = c.m0 + (j & 1) * (kTileRows / 2);
+      if (m0 < tl.seg_rows[c.g]) mx_gemm_tile<kTileRows / 2>(args, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], m0, c.nt, lds);
+    }
+  }
+}
+
+// MXFP8 quantisation of rows x cols values (bf16 or f32), one thread per
+// block of 32: codes [rows, cols] and scale bytes [rows, cols / 32].
+__global__ __launch_bounds__(256) void mx_quantize_kernel(const void* __restrict__ src, int src_bf16, int64_t rows,
+                                                          int cols, uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales) {
+  const int64_t nblk = rows * (cols / 32);
+  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += (int64_t)gridDim.x * blockDim.x) {
+    float v[32];
+    if (src_bf16) {
+      const bf16x8_t* s8 = reinterpret_cast<const bf16x8_t*>(src) + b * 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8_t w = s8[i];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[8 * i + j] = (float)w[j];
+      }
+    } else {
+      const f32x4_t* s4 = reinterpret_cast<const f32x4_t*>(src) + b * 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const f32x4_t w = s4[i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[4 * i + j] = w[j];
+      }
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    const int X = mx_scale(amax);
+    i32x4_t out[2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w |= e4m3_code(ldexpf(v[4 * i + j], -X)) << (8 * j);
+      out[i / 4][i % 4] = (int)w;
+    }
+    *reinterpret_cast<i32x4_t*>(codes + b * 32) = out[0];
+    *reinterpret_cast<i32x4_t*>(codes + b * 32 + 16) = out[1];
+    scales[b] = (uint8_t)(X + 127);
   }
 }
 
@@ -253,6 +331,9 @@ hipError_t launch_grouped_gemm_bf16(const GemmProblem& gp, hipStream_t s) {
   a.s2f = nullptr;
   a.topk = 1;
   a.M = 0;
+  a.c_scale = nullptr;
+  a.a_scale = nullptr;
+  a.w_scale = nullptr;
   const int grid = device_cu_count();
   const int group_cols = grid / kXcds > 0 ? grid / kXcds : 1;
   SplitWs sp{nullptr, nullptr, nullptr};
@@ -270,6 +351,51 @@ hipError_t launch_grouped_gemm_bf16(const GemmProblem& gp, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !sp.hdr) return e;
   grouped_gemm_split_reduce<<<grid, 256, 0, s>>>(a, sp);
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_gemm_mx(const GemmProblem& gp, hipStream_t s) {
+  if (gp.R == 0) return hipSuccess;
+  Bf16GemmArgs a;
+  a.K = gp.K;
+  a.N = gp.N;
+  a.E = gp.E;
+  a.s2f = nullptr;
+  a.topk = 1;
+  a.M = 0;
+  a.c_scale = nullptr;
+  a.a_scale = nullptr;
+  a.w_scale = nullptr;
+  const int grid = device_cu_count();
+  const int group_cols = grid / kXcds > 0 ? grid / kXcds : 1;
+  if (gp.layer == 0) {
+    // x_perm, W_gate, W_up bf16; Hact MXFP8: R*F codes, then R*F/32 scales
+    a.a = (const __bf16*)gp.a;
+    a.w0 = (const __bf16*)gp.w0;
+    a.w1 = (const __bf16*)gp.w1;
+    a.c = gp.c;
+    a.c_scale = reinterpret_cast<uint8_t*>(gp.c) + gp.R * gp.N;
+    grouped_gemm_bf16_kernel<0, true><<<grid, kGemmThreads, 0, s>>>(a, gp.offsets, gp.G, group_cols, SplitWs{});
+  } else {
+    // Hact and W_down MXFP8 (codes, then scales); Y f32
+    a.a = (const __bf16*)gp.a;
+    a.a_scale = reinterpret_cast<const uint8_t*>(gp.a) + gp.R * gp.K;
+    a.w0 = (const __bf16*)gp.w0;
+    a.w_scale = reinterpret_cast<const uint8_t*>(gp.w0) + (int64_t)gp.E * gp.N * gp.K;
+    a.w1 = nullptr;
+    a.c = gp.c;
+    grouped_gemm_mx_kernel<<<grid, kGemmThreads, 0, s>>>(a, gp.offsets, gp.G, group_cols);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_quantize(const void* src, int src_bf16, int64_t rows, int cols, void* dst, hipStream_t s) {
+  const int64_t nblk = rows * (cols / 32);
+  if (nblk == 0) return hipSuccess;
+  uint8_t* codes = reinterpret_cast<uint8_t*>(dst);
+  const int64_t blocks = (nblk + 255) / 256;
+  mx_quantize_kernel<<<(unsigned)(blocks < 65536 ? blocks : 65536), 256, 0, s>>>(src, src_bf16, rows, cols, codes,
+                                                                                  codes + rows * (int64_t)cols);
   return hipGetLastError();
 }
 

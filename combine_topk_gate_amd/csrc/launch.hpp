@@ -54,6 +54,11 @@ struct GemmProblem {
 size_t gemm_split_ws_bytes();
 hipError_t launch_grouped_gemm_bf16(const GemmProblem& gp, hipStream_t s);
 hipError_t launch_grouped_gemm_f32(const GemmProblem& gp, hipStream_t s);
+// MXFP8 activation path: layer 0 bf16 -> Hact MXFP8; layer 1 MXFP8 x MXFP8 -> Y.
+// An MXFP8 tensor of rows x cols is one buffer: codes, then cols/32 scale
+// bytes per row.
+hipError_t launch_grouped_gemm_mx(const GemmProblem& gp, hipStream_t s);
+hipError_t launch_mx_quantize(const void* src, int src_bf16, int64_t rows, int cols, void* dst, hipStream_t s);
 
 hipError_t launch_combine(const float* y, const float* topk_w, const int32_t* flat_to_sorted, int64_t M, int H,
                           int k, const OutEpilogue& ep, hipStream_t s);

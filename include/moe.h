@@ -70,7 +70,16 @@ typedef enum {
   MOE_ERR_DEVICE_TIMEOUT = 5    /* a bounded device wait ran out (fused layer) */
 } moe_status_t;
 
-typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype_t;
+/* MOE_DTYPE_BF16_MXFP8: x, W_gate, W_up and X_perm bf16; the activation
+ * Hact and W_down in MXFP8 ([PTO] two-stage SwiGLU: the activation is
+ * quantised as SwiGLU produces it).  MXFP8 is the OCP microscaling format
+ * with e4m3 elements: per 32 consecutive values of a row one scale byte
+ * s, value = e4m3(code) * 2^(s - 127); the scale is 2^X with X =
+ * floor(log2 of the block's largest magnitude) - 8 (or s = 0 for an
+ * all-zero block), codes are the nearest e4m3 value (ties to even),
+ * magnitudes past 448 become 448.  An MXFP8 tensor of rows x cols is ONE
+ * buffer: rows*cols codes, then rows*cols/32 scale bytes (row-major). */
+typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1, MOE_DTYPE_BF16_MXFP8 = 2 } moe_dtype_t;
 
 /* Operation whose workspace moe_workspace_bytes sizes. */
 typedef enum { MOE_OP_DISPATCH = 0, MOE_OP_GROUPED_GEMM = 1, MOE_OP_LAYER = 2 } moe_op_t;
@@ -81,7 +90,8 @@ typedef enum { MOE_OP_DISPATCH = 0, MOE_OP_GROUPED_GEMM = 1, MOE_OP_LAYER = 2 } 
  * (S*EL <= 1023 when EL < E); R*max(H,F) < 2^31 and EL*H*F < 2^31 (32-bit
  * element offsets).
  * dtype is the type of x, the weights, X_perm and Hact: MOE_DTYPE_BF16
- * (fp32 accumulation) or MOE_DTYPE_F32.  Logits, weights of the top-k and Y
+ * (fp32 accumulation), MOE_DTYPE_F32, or MOE_DTYPE_BF16_MXFP8 (Hact and
+ * W_down MXFP8, the rest bf16; F a multiple of 128).  Logits, weights of the top-k and Y
  * are always f32; out is f32 unless an epilogue asks for bf16.
  *
  * Local experts ([COMET] §4.1.2 tokens grouped by source and expert for
@@ -157,6 +167,10 @@ moe_status_t moe_dispatch(const moe_problem_t* p, const void* x, const int32_t* 
  *   layer 1 ([COMET] §3.2 Layer1; [PTO] GMM2):
  *     a  = Hact [R,F] dtype; w0 = W_down [EL,H,F]; w1 = NULL
  *     c  = Y [R,H] f32: Y[r,n] = sum_f Hact[r,f] W_down[e,n,f], f32 accumulation.
+ *   MOE_DTYPE_BF16_MXFP8: layer 0 writes c as an MXFP8 buffer of R x F
+ *   (the codes decided on the f32 value silu(g) * u), layer 1 reads a (R x
+ *   F) and w0 (EL*H x F) as MXFP8 buffers; the matrix cores multiply the
+ *   codes and apply both block scales, accumulating in f32.  No workspace.
  *   offsets [G+1] int32 as produced by moe_dispatch.  Rows of empty segments
  *   produce nothing.
  *   ws (bf16 layers): NULL, or at least moe_workspace_bytes(p,
@@ -191,7 +205,7 @@ moe_status_t moe_combine(const moe_problem_t* p, const float* y, const float* to
  *   out[t, n] = cast(acc[t, n] + residual[t, n])
  * with one f32 addition (no residual: acc itself) and the cast to out_dtype:
  * f32 keeps the value, bf16 rounds to nearest even.
- *   residual  [M,H] in the problem's dtype (bf16 or f32), or NULL
+ *   residual  [M,H] in the dtype of x (f32 for f32 layers, else bf16), or NULL
  *   out_dtype MOE_DTYPE_F32 or MOE_DTYPE_BF16
  */
 typedef struct {
@@ -259,6 +273,16 @@ moe_status_t moe_layer(const moe_problem_t* p, const void* x, const float* logit
                        const void* w_gate, const void* w_up, const void* w_down, float* out,
                        const moe_layer_aux_t* aux, const moe_layer_opts_t* opts, void* ws, size_t ws_bytes,
                        void* stream);
+
+/*
+ * MXFP8 quantisation (the format of MOE_DTYPE_BF16_MXFP8) of rows x cols
+ * values, blocks of 32 along a row: src [rows, cols] bf16 (src_dtype
+ * MOE_DTYPE_BF16) or f32; dst one buffer of rows*cols + rows*cols/32 bytes
+ * (codes, then scales).  cols a multiple of 32; src and dst 16-byte
+ * aligned.  For W_down, rows = EL*H and cols = F.
+ */
+moe_status_t moe_quantize_mxfp8(int64_t rows, int32_t cols, int32_t src_dtype, const void* src, void* dst,
+                                void* stream);
 
 /* moe_layer with the combine's epilogue (NULL epi: as moe_layer); out [M,H]
  * in epi->out_dtype.  The fused kernel and the chain apply it in the same

@@ -127,21 +127,25 @@ double orc_e4m3_value(uint8_t code) {
   return s ? -v : v;
 }
 
-/* Nearest e4m3 code to v: every non-negative finite code is compared, a tie
- * goes to the even code; magnitudes beyond 448 give 448 (the largest code
- * compared); the sign bit is v's. */
+/* Nearest e4m3 code to v: the non-negative finite codes 0..126 have
+ * increasing values, so the two neighbours of |v| are found by bisection
+ * and the nearer one taken, a tie going to the even code; magnitudes beyond
+ * 448 give 448 (code 126, the largest); the sign bit is v's. */
 uint8_t orc_e4m3_round(double v) {
   double a = fabs(v);
-  int best = 0;
-  double bd = INFINITY;
-  for (int c = 0; c < 127; ++c) {
-    double d = fabs(orc_e4m3_value((uint8_t)c) - a);
-    if (d < bd || (d == bd && (c & 1) == 0)) {
-      bd = d;
-      best = c;
+  int lo = 0, hi = 126; /* invariant: value(lo) <= a, or lo = 0 */
+  if (a >= orc_e4m3_value(126)) {
+    lo = 126;
+  } else {
+    while (hi - lo > 1) {
+      int mid = (lo + hi) / 2;
+      if (orc_e4m3_value((uint8_t)mid) <= a) lo = mid; else hi = mid;
     }
+    /* now value(lo) <= a < value(hi), hi = lo + 1 */
+    double dl = a - orc_e4m3_value((uint8_t)lo), dh = orc_e4m3_value((uint8_t)hi) - a;
+    if (dh < dl || (dh == dl && (hi & 1) == 0)) lo = hi;
   }
-  return (uint8_t)(best | (signbit(v) ? 0x80 : 0));
+  return (uint8_t)(lo | (signbit(v) ? 0x80 : 0));
 }
 
 /*
@@ -178,9 +182,10 @@ static double mx_value(const uint8_t* codes, const uint8_t* scales, int64_t i) {
 int orc_mx_quantize(int64_t rows, int cols, int dtype, const void* src, uint8_t* dst) {
   if (rows < 0 || cols < 32 || cols % 32) return ORC_EINVAL;
   uint8_t* scales = dst + rows * (int64_t)cols;
-  double blk[32];
+#pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < rows; ++r)
     for (int b = 0; b < cols / 32; ++b) {
+      double blk[32];
       for (int i = 0; i < 32; ++i) {
         int64_t idx = r * cols + b * 32 + i;
         blk[i] = dtype < 0 ? ((const double*)src)[idx]

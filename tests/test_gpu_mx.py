@@ -1,0 +1,185 @@
+"""GPU parity of the MXFP8 activation path (dtype bf16_mxfp8): the MXFP8
+quantiser bit for bit, and the layer with Hact and W_down in MXFP8 against
+the oracle's MXFP8 path.
+
+Tolerances.  The weights' codes are decided on the same bf16 values on both
+sides, so they must match bit for bit.  Hact's codes are decided on the f32
+value silu(g) * u, which the GPU accumulates in a different order from the
+oracle's (f64, then rounded to f32): where that value sits at a rounding
+boundary the two codes (or, where the block maximum sits at a power of two,
+the two scales) differ by one step, so each dequantised element must lie
+within one e4m3 step of the larger of the two block scales (2^-3 of the
+magnitude, or 2^(X-9) in the subnormal range), and at least 99.9% of them
+must be equal.  Layer1 is checked on the GPU's own Hact: Y against the f64
+product of its dequantised values and the dequantised W_down, relative
+Frobenius 2e-4 (the matrix cores' fp8 accumulation only).  The whole
+layer against the oracle's MXFP8 layer: relative Frobenius 5e-3, the bf16
+path's bound (one flipped code moves its term by up to 1/16, and a Y
+element sums F terms).  The distance to the bf16 layer is printed: it is
+what MXFP8 costs, not a parity bound.
+"""
+import numpy as np
+import pytest
+import torch
+
+import combine_topk_gate_amd as moe
+import moe_synth
+import oracle
+from moe_gpu_util import host, rel_fro, run_layer, upload
+
+pytestmark = pytest.mark.gpu
+
+
+def _bytes_to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def test_quantizer_bit_exact_against_oracle():
+    rng = np.random.default_rng(201)
+    rows, cols = 96, 256
+    v = (rng.standard_normal((rows, cols)) * np.exp(rng.uniform(-10, 10, (rows, 1)))).astype(np.float32)
+    v[3] = 0.0                                   # all-zero rows
+    v[5, :32] = 448.0                            # exact maximum
+    v[7, :32] = 1e-40                            # below the smallest normal f32
+    v[9, ::2] = -v[9, 1::2]                      # signs
+    pos = np.array([oracle.e4m3_value(c) for c in range(127)])
+    v[11, :126] = ((pos[:-1] + pos[1:]) / 2)[:126] * 2.0 ** -5  # ties after the block scale
+    for src in (v, moe_synth.to_bf16_bits(v)):
+        want = oracle.mx_quantize(src)
+        t = torch.from_numpy(src.view(np.int16)).cuda().view(torch.bfloat16) if src.dtype == np.uint16 else \
+            torch.from_numpy(src).cuda()
+        dst = torch.empty(moe.mx_bytes(rows, cols), dtype=torch.uint8, device="cuda")
+        moe.moe_quantize_mxfp8(t, dst)
+        torch.cuda.synchronize()
+        got = dst.cpu().numpy()
+        assert np.array_equal(got, want), np.nonzero(got != want)[0][:10]
+
+
+def run_chain_mx(cfg, g, wd_mx):
+    """route -> dispatch -> layer 0 (Hact MXFP8) -> layer 1 (MXFP8) -> combine."""
+    p = moe.problem(cfg.M, cfg.H, cfg.F, cfg.E, cfg.k, cfg.S, "bf16_mxfp8", cfg.base, cfg.local)
+    M, k, H, F, G, R = cfg.M, cfg.k, cfg.H, cfg.F, cfg.S * cfg.EL, cfg.M * cfg.k
+    dev = "cuda"
+    o = dict(topk_idx=torch.empty((M, k), dtype=torch.int32, device=dev),
+             topk_w=torch.empty((M, k), dtype=torch.float32, device=dev),
+             counts=torch.empty(G, dtype=torch.int32, device=dev),
+             offsets=torch.empty(G + 1, dtype=torch.int32, device=dev),
+             sorted_to_flat=torch.empty(R, dtype=torch.int32, device=dev),
+             flat_to_sorted=torch.empty(R, dtype=torch.int32, device=dev),
+             x_perm=torch.zeros((R, H), dtype=torch.bfloat16, device=dev),
+             hact=torch.zeros(moe.mx_bytes(R, F), dtype=torch.uint8, device=dev),
+             y=torch.zeros((R, H), dtype=torch.float32, device=dev),
+             out=torch.empty((M, H), dtype=torch.float32, device=dev))
+    ws = torch.empty(max(moe.moe_workspace_bytes(p, moe.MOE_OP_DISPATCH), 4), dtype=torch.uint8, device=dev)
+    assert moe.moe_workspace_bytes(p, moe.MOE_OP_GROUPED_GEMM) == 0
+    moe.moe_route(p, g["logits"], o["topk_idx"], o["topk_w"])
+    moe.moe_dispatch(p, g["x"], o["topk_idx"], g.get("src_block"), o["counts"], o["offsets"], o["sorted_to_flat"],
+                     o["flat_to_sorted"], o["x_perm"], ws)
+    moe.moe_grouped_gemm(p, 0, o["x_perm"], g["w_gate"], g["w_up"], o["offsets"], o["hact"])
+    moe.moe_grouped_gemm(p, 1, o["hact"], wd_mx, None, o["offsets"], o["y"])
+    moe.moe_combine(p, o["y"], o["topk_w"], o["flat_to_sorted"], o["out"])
+    torch.cuda.synchronize()
+    return p, o
+
+
+def _hact_rows(buf, R, F, rows):
+    """Dequantised values and block exponents of the given rows of an MXFP8
+    Hact buffer (numpy uint8)."""
+    codes = buf[:R * F].reshape(R, F)[rows]
+    scales = buf[R * F:].reshape(R, F // 32)[rows]
+    sub = np.concatenate([codes, scales], axis=None)
+    vals = oracle.mx_dequantize(sub, len(rows), F)
+    return vals, scales.astype(np.int64) - 127
+
+
+CASES = {
+    "small": (moe_synth.Config("mx_small", 300, 256, 384, 8, 2, 1, "bf16_mxfp8", 211), None),
+    "qwen2": (moe_synth.config("qwen2", dtype="bf16_mxfp8"), 48),
+    "mixtral": (moe_synth.config("mixtral", dtype="bf16_mxfp8"), 16),
+    "held": (moe_synth.Config("mx_held", 256, 128, 256, 16, 4, 2, "bf16_mxfp8", 213, 0.0, 128, 4, 4), None),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_mx_layer_parity(name):
+    cfg, n_sample = CASES[name]
+    print(f"[mx] {name} {cfg}", flush=True)
+    d = moe_synth.make_inputs(cfg)
+    g = upload(d)
+    EL, H, F = cfg.EL, cfg.H, cfg.F
+    wd_mx_ref = oracle.mx_quantize(d["w_down"].reshape(EL * H, F))
+    wd_mx = torch.empty(moe.mx_bytes(EL * H, F), dtype=torch.uint8, device="cuda")
+    moe.moe_quantize_mxfp8(g["w_down"], wd_mx)
+    torch.cuda.synchronize()
+    assert np.array_equal(wd_mx.cpu().numpy(), wd_mx_ref)
+    print(f"[mx] {name}: W_down quantised, bit-exact", flush=True)
+    p, o = run_chain_mx(cfg, g, wd_mx)
+    toks = None if n_sample is None else moe_synth.token_sample(cfg, n_sample)
+    ref = oracle.moe_layer(d["x"], d["logits"], d["w_gate"], d["w_up"], d["w_down"], cfg.k, S=cfg.S,
+                           src_block=d["src_block"], tokens=toks, want_rows=True, expert_base=cfg.base,
+                           local_experts=cfg.local, w_down_mx=wd_mx_ref)
+    print(f"[mx] {name}: oracle done", flush=True)
+    for key in ("topk_idx", "counts", "offsets", "sorted_to_flat", "flat_to_sorted"):
+        assert np.array_equal(host(o[key]), ref[key]), key
+    tk = np.arange(cfg.M) if toks is None else toks
+    flat = (tk[:, None] * cfg.k + np.arange(cfg.k)[None, :]).reshape(-1)
+    rows = ref["flat_to_sorted"][flat].astype(np.int64)
+    kept = rows >= 0
+    R = cfg.M * cfg.k
+    # Hact: within one e4m3 step of the larger block scale
+    hv, hx = _hact_rows(o["hact"].cpu().numpy(), R, F, rows[kept])
+    rv = ref["hact"][kept]
+    rx = np.zeros_like(hx)
+    for i in range(rv.shape[0]):
+        q = oracle.mx_quantize(rv[i:i + 1])
+        rx[i] = q[F:].astype(np.int64) - 127
+    X = np.repeat(np.maximum(hx, rx), 32, axis=1)
+    step = np.maximum(np.maximum(np.abs(hv), np.abs(rv)) * 2.0 ** -3, 2.0 ** (X - 9))
+    same = np.mean(hv == rv)
+    print(f"[mx] {name}: Hact equal values {same:.5f}, max |d|/step {np.max(np.abs(hv - rv) / step):.3f}")
+    assert np.all(np.abs(hv - rv) <= step * (1 + 1e-12))
+    assert same >= 0.999
+    # Layer1 on the GPU's own Hact: the f64 product with the dequantised weights
+    yg = host(o["y"][torch.from_numpy(rows[kept]).cuda()])
+    offs = ref["offsets"]
+    experts = (np.searchsorted(offs, rows[kept], side="right") - 1) % EL
+    y64 = np.zeros_like(yg)
+    for e in np.unique(experts):
+        sub = np.concatenate([wd_mx_ref[e * H * F:(e + 1) * H * F],
+                              wd_mx_ref[EL * H * F + e * H * (F // 32):EL * H * F + (e + 1) * H * (F // 32)]])
+        w = oracle.mx_dequantize(sub, H, F)
+        sel = experts == e
+        y64[sel] = hv[sel] @ w.T
+        del w
+    e1 = rel_fro(yg, y64)
+    # Y and out against the oracle's MXFP8 layer
+    ey = rel_fro(yg, ref["y"][kept])
+    og = host(o["out"][torch.from_numpy(tk).cuda()])
+    eo = rel_fro(og, ref["out"])
+    bf = oracle.moe_layer(d["x"], d["logits"], d["w_gate"], d["w_up"], d["w_down"], cfg.k, S=cfg.S,
+                          src_block=d["src_block"], tokens=toks, expert_base=cfg.base, local_experts=cfg.local)
+    print(f"[mx] {name}: Layer1 on own Hact relF {e1:.3e}; Y relF {ey:.3e}, out relF {eo:.3e}; "
+          f"distance to the bf16 layer {rel_fro(og, bf['out']):.3e}")
+    assert e1 <= 2e-4
+    assert ey <= 5e-3 and eo <= 5e-3
+    assert rel_fro(og, bf["out"]) <= 0.1  # MXFP8's own error, a sanity bound only
+    # moe_layer runs this dtype as the same chain
+    out, _, st = run_layer(cfg, dict(g, w_down=wd_mx))
+    assert st == 0 and torch.equal(out, o["out"])
+
+
+def test_mx_combine_epilogue_reads_a_bf16_residual():
+    """The residual of an MXFP8 layer is in x's dtype (bf16): the epilogue
+    equals the f32 combine plus the residual, cast by torch, bit for bit."""
+    cfg = moe_synth.Config("mx_epi", 256, 256, 256, 8, 2, 1, "bf16_mxfp8", 215)
+    d = moe_synth.make_inputs(cfg)
+    g = upload(d)
+    wd_mx = torch.empty(moe.mx_bytes(cfg.E * cfg.H, cfg.F), dtype=torch.uint8, device="cuda")
+    moe.moe_quantize_mxfp8(g["w_down"], wd_mx)
+    p, o = run_chain_mx(cfg, g, wd_mx)
+    res = torch.randn(cfg.M, cfg.H, generator=torch.Generator().manual_seed(7)).to(torch.bfloat16).cuda()
+    out = torch.empty(cfg.M, cfg.H, dtype=torch.bfloat16, device="cuda")
+    moe.moe_combine_ex(p, o["y"], o["topk_w"], o["flat_to_sorted"], moe.epilogue(res, "bf16"), out)
+    torch.cuda.synchronize()
+    want = (o["out"] + res.float()).to(torch.bfloat16)
+    assert torch.equal(out.view(torch.int16), want.view(torch.int16))

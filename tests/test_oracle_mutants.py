@@ -46,7 +46,9 @@ MUTANTS = {
                                   "double v = acc[i];"),
     "epilogue_not_rounded": ("out[i] = (out_dtype == ORC_BF16) ? orc_round_to_bf16(v) : v;", "out[i] = v;"),
     "mx_scale_exponent_off_by_one": ("X = e - 1 - 8;", "X = e - 8;"),
-    "mx_ties_to_odd": ("if (d < bd || (d == bd && (c & 1) == 0)) {", "if (d < bd || (d == bd && (c & 1) == 1)) {"),
+    "mx_ties_to_odd": ("if (dh < dl || (dh == dl && (hi & 1) == 0)) lo = hi;",
+                       "if (dh < dl || (dh == dl && (hi & 1) == 1)) lo = hi;"),
+    "mx_rounds_down": ("if (dh < dl || (dh == dl && (hi & 1) == 0)) lo = hi;", ""),
     "mx_amax_skips_last": ("for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs(v[i]));",
                            "for (int i = 0; i < 31; ++i) amax = fmax(amax, fabs(v[i]));"),
     "mx_down_scale_index": ("acc += hact[f] * mx_value(wc + wrow, ws + wrow / 32, f);",

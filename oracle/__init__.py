@@ -53,6 +53,7 @@ def _configure(lib):
     lib.orc_e4m3_round.restype = ctypes.c_uint8
     lib.orc_mx_quantize.argtypes = [I64, I32, I32, P, P]
     lib.orc_mx_dequantize.argtypes = [I64, I32, P, P]
+    lib.orc_mx_scales.argtypes = [I64, I32, P, P]
     lib.orc_combine_tokens.argtypes = [I32, I32, I64, P, P, P, P]
     lib.orc_epilogue.argtypes = [I64, P, P, I32, I32, P]
     lib.orc_moe_layer.argtypes = [I64, I32, I32, I32, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, I64, P,
@@ -60,7 +61,7 @@ def _configure(lib):
     lib.orc_num_threads.argtypes = []
     for name in ("orc_route", "orc_counts_offsets", "orc_permutation", "orc_dispatch",
                  "orc_ffn_rows", "orc_combine_tokens", "orc_epilogue", "orc_moe_layer", "orc_num_threads",
-                 "orc_mx_quantize", "orc_mx_dequantize"):
+                 "orc_mx_quantize", "orc_mx_dequantize", "orc_mx_scales"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -200,14 +201,20 @@ def e4m3_round(v: float) -> int:
     return int(_load().orc_e4m3_round(float(v)))
 
 
+def mx_bytes(rows, cols):
+    """Bytes of an MX buffer: the codes, then the scales in groups of 32 rows."""
+    return rows * cols + (rows + 31) // 32 * 32 * (cols // 32)
+
+
 def mx_quantize(values):
     """MXFP8 quantisation of a [rows, cols] array (f32, bf16 bits or f64;
-    cols a multiple of 32) in blocks of 32 along a row: one uint8 buffer of
-    rows*cols e4m3 codes followed by rows*cols/32 scale bytes."""
+    cols a multiple of 128) in blocks of 32 along a row: one uint8 buffer of
+    rows*cols e4m3 codes followed by the scale bytes (groups of 32 rows, per
+    128-column quad the 4 bytes of each row)."""
     v = np.ascontiguousarray(values)
     rows, cols = v.shape[0], int(np.prod(v.shape[1:]))
     dt = -1 if v.dtype == np.float64 else _dtype_code(v)
-    out = np.empty(rows * cols + rows * cols // 32, np.uint8)
+    out = np.empty(mx_bytes(rows, cols), np.uint8)
     _check(_load().orc_mx_quantize(rows, cols, dt, _p(v), _p(out)), "mx_quantize")
     return out
 
@@ -217,6 +224,14 @@ def mx_dequantize(buf, rows, cols):
     b = _c(buf, np.uint8)
     out = np.empty((rows, cols), np.float64)
     _check(_load().orc_mx_dequantize(rows, cols, _p(b), _p(out)), "mx_dequantize")
+    return out
+
+
+def mx_scales(buf, rows, cols):
+    """Scale bytes of an MXFP8 buffer as a [rows, cols/32] uint8 array."""
+    b = _c(buf, np.uint8)
+    out = np.empty((rows, cols // 32), np.uint8)
+    _check(_load().orc_mx_scales(rows, cols, _p(b), _p(out)), "mx_scales")
     return out
 
 
@@ -289,7 +304,7 @@ def moe_layer(x, logits, w_gate, w_up, w_down, k, S=1, src_block=None, tokens=No
     if w_down_mx is not None:
         act_fp8 = 1
         wd = _c(w_down_mx, np.uint8)
-        assert wd.size == EL * H * F + EL * H * F // 32
+        assert wd.size == mx_bytes(EL * H, F)
     src_block = _c(src_block, np.int32)
     tok = None if tokens is None else _c(tokens, np.int64)
     n_tok = M if tok is None else tok.shape[0]

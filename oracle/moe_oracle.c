@@ -169,19 +169,35 @@ static void mx_block(const double* v, uint8_t* codes, uint8_t* scale) {
   *scale = (uint8_t)(X + 127);
 }
 
-/* Value of element i of an MX row (codes, and one scale byte per 32). */
-static double mx_value(const uint8_t* codes, const uint8_t* scales, int64_t i) {
-  return ldexp(orc_e4m3_value(codes[i]), (int)scales[i / 32] - 127);
+/*
+ * Storage of an MX tensor of rows x cols (cols a multiple of 128), the
+ * library's buffer format: the codes row by row, then the scale bytes in
+ * groups of 32 rows (the last group padded to 32): for row group g and
+ * column quad q (columns 128 q .. 128 q + 127, blocks 4 q .. 4 q + 3), 128
+ * bytes hold the 4 scale bytes of each of the group's rows, row by row.
+ * This is a storage convention only (a kernel reads one stage's scales of
+ * 32 rows as 128 contiguous bytes); the values are those of mx_block.
+ */
+static int64_t mx_scale_index(int64_t r, int b, int cols) {
+  return ((r / 32) * (cols / 128) + b / 4) * 128 + (r % 32) * 4 + (b % 4);
+}
+
+static int64_t mx_scale_bytes(int64_t rows, int cols) { return (rows + 31) / 32 * 32 * (cols / 32); }
+
+/* Value of element (r, c) of an MX tensor of `cols` columns. */
+static double mx_value(const uint8_t* codes, const uint8_t* scales, int64_t r, int c, int cols) {
+  return ldexp(orc_e4m3_value(codes[r * cols + c]), (int)scales[mx_scale_index(r, c / 32, cols)] - 127);
 }
 
 /*
- * Quantise rows x cols values (cols a multiple of 32; f32 or bf16 bits, or
- * doubles when dtype is -1) into one buffer: rows*cols codes, then
- * rows*cols/32 scale bytes, row-major, the layout the down weights take.
+ * Quantise rows x cols values (cols a multiple of 128; f32 or bf16 bits, or
+ * doubles when dtype is -1) into one buffer: rows*cols codes, then the
+ * scale bytes as above (padding bytes 0).
  */
 int orc_mx_quantize(int64_t rows, int cols, int dtype, const void* src, uint8_t* dst) {
-  if (rows < 0 || cols < 32 || cols % 32) return ORC_EINVAL;
+  if (rows < 0 || cols < 128 || cols % 128) return ORC_EINVAL;
   uint8_t* scales = dst + rows * (int64_t)cols;
+  memset(scales, 0, (size_t)mx_scale_bytes(rows, cols));
 #pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < rows; ++r)
     for (int b = 0; b < cols / 32; ++b) {
@@ -192,17 +208,26 @@ int orc_mx_quantize(int64_t rows, int cols, int dtype, const void* src, uint8_t*
                            : (dtype == ORC_F32 ? (double)((const float*)src)[idx]
                                                : orc_bf16_bits_to_double(((const uint16_t*)src)[idx]));
       }
-      mx_block(blk, dst + r * cols + b * 32, scales + r * (cols / 32) + b);
+      mx_block(blk, dst + r * cols + b * 32, scales + mx_scale_index(r, b, cols));
     }
   return ORC_OK;
 }
 
 /* Values of a quantised buffer (rows x cols) as doubles. */
 int orc_mx_dequantize(int64_t rows, int cols, const uint8_t* src, double* out) {
-  if (rows < 0 || cols < 32 || cols % 32) return ORC_EINVAL;
+  if (rows < 0 || cols < 128 || cols % 128) return ORC_EINVAL;
   const uint8_t* scales = src + rows * (int64_t)cols;
   for (int64_t r = 0; r < rows; ++r)
-    for (int c = 0; c < cols; ++c) out[r * cols + c] = mx_value(src + r * cols, scales + r * (cols / 32), c);
+    for (int c = 0; c < cols; ++c) out[r * cols + c] = mx_value(src, scales, r, c, cols);
+  return ORC_OK;
+}
+
+/* Scale bytes of an MX tensor as a rows x cols/32 array (row-major). */
+int orc_mx_scales(int64_t rows, int cols, const uint8_t* src, uint8_t* out) {
+  if (rows < 0 || cols < 128 || cols % 128) return ORC_EINVAL;
+  const uint8_t* scales = src + rows * (int64_t)cols;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int b = 0; b < cols / 32; ++b) out[r * (cols / 32) + b] = scales[mx_scale_index(r, b, cols)];
   return ORC_OK;
 }
 
@@ -361,8 +386,8 @@ static void ffn_row(int H, int F, int dtype, int act_fp8, int E, const double* x
     const uint8_t* ws = wc + (int64_t)E * H * F;
     for (int n = 0; n < H; ++n) {
       double acc = 0.0;
-      int64_t wrow = eHF + (int64_t)n * F;
-      for (int f = 0; f < F; ++f) acc += hact[f] * mx_value(wc + wrow, ws + wrow / 32, f);
+      int64_t wrow = (int64_t)e * H + n; /* row of the [E*H, F] tensor */
+      for (int f = 0; f < F; ++f) acc += hact[f] * mx_value(wc, ws, wrow, f, F);
       y[n] = acc;
     }
     return;
@@ -392,7 +417,7 @@ int orc_ffn_rows(int H, int F, int E, int S, int k, int dtype, int act_fp8, cons
                  const void* w_up, const void* w_down, const int32_t* sorted_to_flat, const int32_t* offsets,
                  int64_t n_rows, const int64_t* rows, double* hact_out, double* y_out) {
   if (H < 1 || F < 1 || E < 1 || S < 1 || k < 1 || (dtype != ORC_F32 && dtype != ORC_BF16)) return ORC_EINVAL;
-  if (act_fp8 && F % 32) return ORC_EINVAL;
+  if (act_fp8 && F % 128) return ORC_EINVAL;
   int64_t G = (int64_t)S * E;
   int bad = 0;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)

@@ -51,8 +51,10 @@ MUTANTS = {
     "mx_rounds_down": ("if (dh < dl || (dh == dl && (hi & 1) == 0)) lo = hi;", ""),
     "mx_amax_skips_last": ("for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs(v[i]));",
                            "for (int i = 0; i < 31; ++i) amax = fmax(amax, fabs(v[i]));"),
-    "mx_down_scale_index": ("acc += hact[f] * mx_value(wc + wrow, ws + wrow / 32, f);",
-                            "acc += hact[f] * mx_value(wc + wrow, ws + wrow, f);"),
+    "mx_down_scale_index": ("int64_t wrow = (int64_t)e * H + n;", "int64_t wrow = (int64_t)n;"),
+    "mx_value_wrong_block": ("scales[mx_scale_index(r, c / 32, cols)]", "scales[mx_scale_index(r, c / 128, cols)]"),
+    "mx_layout_transposed": ("return ((r / 32) * (cols / 128) + b / 4) * 128 + (r % 32) * 4 + (b % 4);",
+                             "return ((r / 32) * (cols / 128) + b / 4) * 128 + (b % 4) * 32 + (r % 32);"),
     "mx_act_not_quantised": ("for (int i = 0; i < 32; ++i) hact[b * 32 + i] = ldexp(orc_e4m3_value(codes[i]), (int)sc - 127);",
                              ""),
     "epilogue_rounds_acc_first": ("double v = acc[i] + (residual ? load_elem(residual, res_dtype, i) : 0.0);",
@@ -93,6 +95,7 @@ def _checks():
         ("e4m3_clamp", pins.test_e4m3_rounding_clamps_to_448),
         ("mx_hand", pins.test_mx_block_hand_values),
         ("mx_round_trip", pins.test_mx_round_trip_within_half_a_step),
+        ("mx_layout", pins.test_mx_scale_storage_layout),
         ("mx_layer", pins.test_mx_layer_matches_dense_quantised_evaluation),
     ]
 

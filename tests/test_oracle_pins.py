@@ -423,8 +423,10 @@ def test_e4m3_rounding_clamps_to_448():
 
 def test_mx_block_hand_values():
     def q(block):
-        buf = oracle.mx_quantize(np.asarray(block, np.float64).reshape(1, 32))
-        return buf[:32], int(buf[32])
+        # one row of 128 values: the block under test, then three zero blocks
+        buf = oracle.mx_quantize(np.concatenate([np.asarray(block, np.float64), np.zeros(96)]).reshape(1, 128))
+        assert np.all(buf[32:128] == 0) and buf.size == 128 + 32 * 4 and np.all(buf[129:] == 0)
+        return buf[:32], int(buf[128])
     codes, s = q([1.0] * 32)            # floor(log2 1) - 8 = -8: 1 / 2^-8 = 256 = code 0x78
     assert s == 127 - 8 and np.all(codes == 0x78)
     codes, s = q([448.0] + [0.0] * 31)  # X = 0, 448 exact
@@ -443,7 +445,7 @@ def test_mx_round_trip_within_half_a_step():
     v = rng.standard_normal((64, 256)) * np.exp(rng.uniform(-8, 8, (64, 1)))
     buf = oracle.mx_quantize(v)
     d = oracle.mx_dequantize(buf, 64, 256)
-    scales = buf[64 * 256:].astype(np.int64).reshape(64, 8)
+    scales = oracle.mx_scales(buf, 64, 256).astype(np.int64)
     X = np.repeat(scales - 127, 32, axis=1)
     t = np.abs(v) / 2.0 ** X                      # magnitude in units of the block scale
     assert np.all(t.reshape(64, 8, 32).max(axis=2) >= 256) and np.all(t < 512)
@@ -454,6 +456,32 @@ def test_mx_round_trip_within_half_a_step():
     assert np.all(np.abs(d[clamped]) == 448 * 2.0 ** X[clamped])
     # values already on the grid come back exactly
     assert np.array_equal(oracle.mx_dequantize(oracle.mx_quantize(d), 64, 256), d)
+
+
+def test_mx_scale_storage_layout():
+    """The buffer format (a storage convention of the library, not of the
+    format): codes row-major, then for each group of 32 rows (the last one
+    padded with zero bytes) and each 128-column quad, the 4 scale bytes of
+    each row in turn.  Every block here gets its own power of two, so its
+    scale byte names it: block (r, b) holds 2^(r + 2b - 40) * 256."""
+    rows, cols = 40, 256
+    r_, b_ = np.meshgrid(np.arange(rows), np.arange(cols // 32), indexing="ij")
+    X = r_ + 2 * b_ - 40
+    v = np.repeat(2.0 ** X * 256, 32, axis=1)
+    buf = oracle.mx_quantize(v)
+    assert buf.size == rows * cols + 64 * 8        # two groups of 32 rows, 8 blocks each
+    assert np.all(buf[:rows * cols] == 0x78)        # 256 in units of the scale = 1.0 * 2^8
+    sc = buf[rows * cols:]
+    for r in range(rows):
+        for b in range(cols // 32):
+            g, q = divmod(r, 32)[0], b // 4
+            pos = (g * 2 + q) * 128 + (r % 32) * 4 + b % 4
+            assert sc[pos] == 127 + X[r, b], (r, b)
+    # padding rows 40..63 of the second group
+    for q in range(2):
+        blk = sc[(2 + q) * 128:(3 + q) * 128].reshape(32, 4)
+        assert np.all(blk[8:] == 0)
+    assert np.array_equal(oracle.mx_scales(buf, rows, cols), (127 + X).astype(np.uint8))
 
 
 def test_mx_layer_matches_dense_quantised_evaluation():

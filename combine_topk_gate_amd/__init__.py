@@ -117,8 +117,10 @@ _DTYPES = {"bf16": MOE_DTYPE_BF16, "f32": MOE_DTYPE_F32, "bf16_mxfp8": MOE_DTYPE
 
 
 def mx_bytes(rows: int, cols: int) -> int:
-    """Bytes of an MXFP8 buffer of rows x cols (codes, then one scale per 32)."""
-    return rows * cols + rows * cols // 32
+    """Bytes of an MXFP8 buffer of rows x cols (cols a multiple of 128): the
+    codes, then one scale byte per 32 values with rows padded to a multiple
+    of 32."""
+    return rows * cols + (rows + 31) // 32 * 32 * (cols // 32)
 
 
 def problem(M, H, F, E, k, S=1, dtype="bf16", expert_base=0, local_experts=0) -> Problem:

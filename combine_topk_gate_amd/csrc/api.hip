@@ -22,7 +22,7 @@ size_t elem_bytes(const moe_problem_t* p) { return p->dtype == MOE_DTYPE_F32 ? 4
 bool is_mx(const moe_problem_t* p) { return p->dtype == MOE_DTYPE_BF16_MXFP8; }
 // bytes of the Hact buffer: R x F elements, or an MXFP8 buffer (codes + scales)
 size_t hact_bytes(const moe_problem_t* p, int64_t R) {
-  return is_mx(p) ? (size_t)R * p->ffn + (size_t)R * (p->ffn / 32) : (size_t)R * p->ffn * elem_bytes(p);
+  return is_mx(p) ? (size_t)R * p->ffn + (size_t)mx_scale_bytes(R, p->ffn) : (size_t)R * p->ffn * elem_bytes(p);
 }
 
 // Experts held by the call (weights it is given): EL, or all E.
@@ -373,7 +373,7 @@ moe_status_t moe_layer(const moe_problem_t* p, const void* x, const float* logit
 
 moe_status_t moe_quantize_mxfp8(int64_t rows, int32_t cols, int32_t src_dtype, const void* src, void* dst,
                                 void* stream) {
-  if (rows < 0 || cols < 32 || cols % 32) return MOE_ERR_INVALID_ARGUMENT;
+  if (rows < 0 || cols < 128 || cols % 128) return MOE_ERR_INVALID_ARGUMENT;
   if (src_dtype != MOE_DTYPE_BF16 && src_dtype != MOE_DTYPE_F32) return MOE_ERR_INVALID_ARGUMENT;
   if (rows == 0) return MOE_OK;
   if (!src || !dst || !aligned(src, 16) || !aligned(dst, 16)) return MOE_ERR_INVALID_ARGUMENT;

@@ -54,6 +54,13 @@ __device__ __forceinline__ int mx_scale(float amax) {
   return X < -127 ? -127 : X;
 }
 
+// Scale bytes of an MXFP8 tensor of rows x cols (cols a multiple of 128):
+// one per 32 values, rows padded to a multiple of 32 (groups of 32 rows;
+// per group and 128-column quad, the 4 bytes of each row in turn).
+__host__ __device__ __forceinline__ int64_t mx_scale_bytes(int64_t rows, int64_t cols) {
+  return (rows + 31) / 32 * 32 * (cols / 32);
+}
+
 // e4m3 code of v (already divided by the block scale, |v| < 512): round to
 // nearest, ties to even, magnitudes past 448 give 448 (0x7E); sign of v.
 // Normal range (|v| >= 2^-6): v = 2^E (1 + m/8), code (E + 7) * 8 + m, where

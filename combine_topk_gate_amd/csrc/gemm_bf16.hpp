@@ -54,12 +54,15 @@ struct Bf16GemmArgs {
   const __bf16* w0;  // layer 0: W_gate [E, F, H]; layer 1: W_down [E, H, F]
   const __bf16* w1;  // layer 0: W_up [E, F, H]
   void* c;           // layer 0: Hact [R, F] bf16 (or MXFP8 codes); layer 1: Y [R, H] f32
-  // MXFP8 (one e8m0 scale byte per 32 values along the reduction index):
-  // layer 0 writes Hact's scales [R, F/32] here; layer 1 reads the token
-  // rows' and the weights' scales ([R, F/32] and [E, H, F/32])
+  // MXFP8 (one e8m0 scale byte per 32 values along the reduction index,
+  // stored in groups of 32 rows: the byte of row r, block b of a tensor of
+  // `cols` columns sits at (r / 32) * cols + (b / 4) * 128 + (r % 32) * 4 +
+  // b % 4): layer 0 writes Hact's scales here; layer 1 reads the token rows'
+  // and the weights' scales (regions of a_scale_bytes and w_scale_bytes)
   uint8_t* c_scale;
   const uint8_t* a_scale;
   const uint8_t* w_scale;
+  uint32_t a_scale_bytes, w_scale_bytes;
   int K, N, E;
   // gather mode (layer 0 inside the fused layer): sorted row r reads token
   // row sorted_to_flat[r] / topk of x directly, so X_perm is never written
@@ -465,7 +468,8 @@ __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int
         uint8_t* dst = hact + (int64_t)(seg_start + trow) * N + f;
         *reinterpret_cast<i32x4_t*>(dst) = out[0];
         *reinterpret_cast<i32x4_t*>(dst + 16) = out[1];
-        p.c_scale[(int64_t)(seg_start + trow) * (N / 32) + f / 32] = (uint8_t)(X + 127);
+        const int64_t r = seg_start + trow;
+        p.c_scale[(r >> 5) * N + col0 + (r & 31) * 4 + b] = (uint8_t)(X + 127);
       }
     }
     __syncthreads();

@@ -4,7 +4,10 @@
 // produces it and the down product consumes the quantised values.  Both
 // operands are in the OCP microscaling format MXFP8: e4m3 codes and one
 // power-of-two scale byte per 32 values along the reduction index F (Hact
-// [R, F] with scales [R, F/32]; W_down [E, H, F] with scales [E, H, F/32]).
+// [R, F], W_down [E, H, F] as [E*H, F]).  The scale bytes are stored in
+// groups of 32 rows: per group and 128-column quad (one stage), the 4 bytes
+// of each row in turn, so the scales of 32 fragment rows for a stage are
+// one 128-byte line.
 // v_mfma_scale_f32_32x32x64_f8f6f4 multiplies the codes and applies both
 // operands' block scales itself, so nothing is dequantised in registers.
 //
@@ -49,7 +52,6 @@ __device__ __forceinline__ void mx_gemm_tile(const Bf16GemmArgs& p, int g, int s
   const int e = g % p.E;
   const int K = p.K, N = p.N;  // K = F (bytes per row), N = H
   const uint32_t row_bytes = (uint32_t)K;
-  const uint32_t srow_bytes = (uint32_t)K / 32u;  // scale bytes per row
 
   const int lc = tid & 7, lr = tid >> 3;
   const int col0 = nt * kL1Cols;
@@ -59,11 +61,10 @@ __device__ __forceinline__ void mx_gemm_tile(const Bf16GemmArgs& p, int g, int s
   const uint8_t* xcodes = reinterpret_cast<const uint8_t*>(p.a);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(wcodes + ((int64_t)e * N + col0) * K, (uint32_t)ncols * row_bytes);
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(xcodes + (int64_t)(seg_start + m0) * K, (uint32_t)trows * row_bytes);
-  // scale rows; rows past the range read 0 (their codes read 0 as well)
-  const __amdgpu_buffer_rsrc_t rws =
-      make_rsrc(p.w_scale + ((int64_t)e * N + col0) * (K / 32), (uint32_t)ncols * srow_bytes);
-  const __amdgpu_buffer_rsrc_t rxs =
-      make_rsrc(p.a_scale + (int64_t)(seg_start + m0) * (K / 32), (uint32_t)trows * srow_bytes);
+  // whole scale regions; a fragment row past the tile's rows takes an
+  // offset past the region and reads scale 0 (its codes read 0 as well)
+  const __amdgpu_buffer_rsrc_t rws = make_rsrc(p.w_scale, p.w_scale_bytes);
+  const __amdgpu_buffer_rsrc_t rxs = make_rsrc(p.a_scale, p.a_scale_bytes);
   const uint32_t voff0 = (uint32_t)lr * row_bytes + (uint32_t)lc * 16u;
   const uint32_t vstep = 32u * row_bytes;
   const uint32_t st_off = (uint32_t)lr * 128u + ((uint32_t)(lc ^ (lr & 7) ^ ((lr >> 3) & 1)) << 4);
@@ -114,15 +115,25 @@ __device__ __forceinline__ void mx_gemm_tile(const Bf16GemmArgs& p, int g, int s
   };
 
   // scale dwords (blocks 4 kt .. 4 kt + 3 of the lane's rows), shifted so
-  // byte 2 kk is block 4 kt + 2 kk + lk
+  // byte 2 kk is block 4 kt + 2 kk + lk.  Row r's dword of stage kt is at
+  // (r / 32) * K + kt * 128 + (r % 32) * 4; the fragment rows of one lane
+  // group are 32 consecutive rows, so a load covers one or two lines.
   uint32_t sw[4], sx[NJ], sw_n[4], sx_n[NJ];
   uint32_t sw_off[4], sx_off[NJ];
+  constexpr uint32_t kNoRow = 0xC0000000u;  // past any scale region
+  auto soffset = [&](int64_t r) { return (uint32_t)((r >> 5) * K + (r & 31) * 4); };
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) sw_off[mi] = (uint32_t)(wn * 128 + mi * 32 + lrow) * srow_bytes;
+  for (int mi = 0; mi < 4; ++mi) {
+    const int lr_ = wn * 128 + mi * 32 + lrow;
+    sw_off[mi] = lr_ < ncols ? soffset((int64_t)e * N + col0 + lr_) : kNoRow;
+  }
 #pragma unroll
-  for (int nj = 0; nj < NJ; ++nj) sx_off[nj] = (uint32_t)(wm * (TM / 2) + nj * 32 + lrow) * srow_bytes;
+  for (int nj = 0; nj < NJ; ++nj) {
+    const int lr_ = wm * (TM / 2) + nj * 32 + lrow;
+    sx_off[nj] = lr_ < trows ? soffset((int64_t)seg_start + m0 + lr_) : kNoRow;
+  }
   auto sload = [&](uint32_t* dw, uint32_t* dx, int kt) {
-    const uint32_t soff = (uint32_t)kt * 4u;
+    const uint32_t soff = (uint32_t)kt * 128u;
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) dw[mi] = buf_load4(rws, sw_off[mi], soff) >> (8 * lk);
 #pragma unroll
@@ -151,25 +162,51 @@ __device__ __forceinline__ void mx_gemm_tile(const Bf16GemmArgs& p, int g, int s
   };
 
   const int nk = uniform(K / 128);
-  // prologue: stage 0 into LDS, stage 1 into registers (loads in the loop's
-  // order: weights, then tokens), scales of stage 0, fragments of (0, 0)
+  // prologue: stage 0 into LDS, then the scales of stage 0 and stage 1 into
+  // registers, each load fenced so they issue in the loop body's order
+  // (scales, weights, tokens): the wait-count pass merges the prologue with
+  // the loop's back edge at the loop header, and any other order makes every
+  // iteration wait for loads it does not need yet
   gload(0);
   lstore(0);
-  sload(sw, sx, 0);
-  gload(nk > 1 ? 1 : 0);
+  {
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      sw[mi] = buf_load4(rws, sw_off[mi], 0) >> (8 * lk);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int nj = 0; nj < NJ; ++nj) {
+      sx[nj] = buf_load4(rxs, sx_off[nj], 0) >> (8 * lk);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const uint32_t soff = (uint32_t)(nk > 1 ? 1 : 0) * 128u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      wreg[i] = buf_load16(rw, voff0 + (uint32_t)i * vstep, soff);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 0; i < XI; ++i) {
+      xreg[i] = buf_load16(rx, voff0 + (uint32_t)i * vstep, soff);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
   __syncthreads();
   read_frags(0, 0, 0);
 
   if constexpr (TM == kTileRows) {
-    // Iteration kt.  Sub-step 0 (16 MFMAs on fragment set 0): after each
-    // MFMA one fragment read of sub-step 1 (set 1), one LDS store of stage
-    // kt+1 into the other buffer, and one load: the 8 scale dwords of stage
-    // kt+1 first (so waiting for them never waits for the data loads issued
-    // after), then the 8 weight loads of stage kt+2.  Barrier.  Sub-step 1
-    // (set 1): after each MFMA one read of stage kt+1's first fragments
-    // (set 0) and, for the first 8, the token loads of stage kt+2.  The
-    // order is pinned with scheduling groups: one wave per SIMD cannot hide
-    // a burst of memory operations behind another wave.
+    // Iteration kt, as in the bf16 tile: sub-step 0 (16 MFMAs on fragment
+    // set 0) with, after each MFMA, one read of sub-step 1's fragments (set
+    // 1), one of the first 8 LDS stores of stage kt+1 into the other buffer
+    // and one load (the 8 scale dwords of kt+1 first, so waiting for them
+    // never waits for the data loads issued after; then the weights of
+    // kt+2).  Sub-step 1: the last 8 stores beside the first 8 MFMAs, the
+    // barrier, then stage kt+1's first fragments (into set 0, free by now)
+    // and the token loads beside the last 8 MFMAs, so the matrix cores keep
+    // working across the barrier.  The order is pinned with scheduling
+    // groups: one wave per SIMD cannot hide a burst of memory operations
+    // behind another wave.
     constexpr int NR = 2 * (4 + NJ);  // 16-byte fragment reads per sub-step
     auto read_one = [&](int set, int stage, int kk, int j) {
       // fragments in the order the MFMAs use them: weight 0, the token
@@ -192,15 +229,30 @@ __device__ __forceinline__ void mx_gemm_tile(const Bf16GemmArgs& p, int g, int s
       else
         *reinterpret_cast<i32x4_t*>(wdst + kOperandBytes + (i - 8) * 4096) = xreg[i - 8];
     };
+    auto mfma_half = [&](int set, int kk, int h) {  // weight fragments 2h, 2h + 1
+#pragma unroll
+      for (int mi = 2 * h; mi < 2 * h + 2; ++mi) {
+        const int sa = (int)((sw[mi] >> (16 * kk)) & 0xFFu);
+#pragma unroll
+        for (int nj = 0; nj < NJ; ++nj) {
+          const int sb = (int)((sx[nj] >> (16 * kk)) & 0xFFu);
+          acc[mi][nj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[set][mi], fb[set][nj], acc[mi][nj], 0, 0, 0,
+                                                                       sa, 0, sb);
+        }
+      }
+    };
     for (int kt = 0; kt < nk; ++kt) {
       const int cur = kt & 1, nxt = cur ^ 1;
       const int kload = (kt + 2 < nk) ? kt + 2 : nk - 1;
       const uint32_t soff = (uint32_t)kload * 128u;
-      const uint32_t ssoff = (uint32_t)((kt + 1 < nk) ? kt + 1 : nk - 1) * 4u;
+      const uint32_t ssoff = (uint32_t)((kt + 1 < nk) ? kt + 1 : nk - 1) * 128u;
+      // sub-step 0: after each MFMA one read (set 1), one store (the first
+      // 8 of stage kt+1) or none, and one load (scales of kt+1, then the
+      // weights of kt+2)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         read_one(1, cur, 1, i);
-        store_one(nxt, i);
+        if (i < 8) store_one(nxt, i);
         if (i < 4)
           sw_n[i] = buf_load4(rws, sw_off[i], ssoff) >> (8 * lk);
         else if (i < 8)
@@ -213,23 +265,34 @@ __device__ __forceinline__ void mx_gemm_tile(const Bf16GemmArgs& p, int g, int s
       for (int i = 0; i < 16; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+        if (i < 8) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // sub-step 1, first half (weights 0, 1): the last 8 stores
+#pragma unroll
+      for (int i = 8; i < 16; ++i) store_one(nxt, i);
+      mfma_half(1, 1, 0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
       }
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
+      // sub-step 1, second half (weights 2, 3): stage kt+1's first fragments
+      // into the free set 0, and the token loads of kt+2
 #pragma unroll
-      for (int i = 0; i < NR; ++i) {
-        read_one(0, nxt, 0, i);
-        if (i < XI) xreg[i] = buf_load16(rx, voff0 + (uint32_t)i * vstep, soff);
-      }
-      mfmas(1, 1);
+      for (int i = 0; i < NR; ++i) read_one(0, nxt, 0, i);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
+      for (int i = 0; i < XI; ++i) xreg[i] = buf_load16(rx, voff0 + (uint32_t)i * vstep, soff);
+      mfma_half(1, 1, 1);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-        if (i < XI) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll

@@ -146,13 +146,24 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_mx_kernel(Bf16GemmA
   }
 }
 
-// MXFP8 quantisation of rows x cols values (bf16 or f32), one thread per
-// block of 32: codes [rows, cols] and scale bytes [rows, cols / 32].
+// MXFP8 quantisation of rows x cols values (bf16 or f32; cols a multiple of
+// 128), one thread per scale byte, in storage order: codes [rows, cols];
+// scale bytes in groups of 32 rows (rows padded to a multiple of 32; the
+// padding's bytes are 0), for each 128-column quad the 4 bytes of each row.
 __global__ __launch_bounds__(256) void mx_quantize_kernel(const void* __restrict__ src, int src_bf16, int64_t rows,
                                                           int cols, uint8_t* __restrict__ codes,
                                                           uint8_t* __restrict__ scales) {
-  const int64_t nblk = rows * (cols / 32);
-  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += (int64_t)gridDim.x * blockDim.x) {
+  const int64_t nblk = (rows + 31) / 32 * 32 * (cols / 32);
+  for (int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; s < nblk; s += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t grp = s / cols;
+    const int in = (int)(s - grp * cols);  // byte inside the group's cols bytes
+    const int64_t r = grp * 32 + ((in & 127) >> 2);
+    const int j = (in >> 7) * 4 + (in & 3);  // block of row r
+    if (r >= rows) {
+      scales[s] = 0;
+      continue;
+    }
+    const int64_t b = r * (cols / 32) + j;
     float v[32];
     if (src_bf16) {
       const bf16x8_t* s8 = reinterpret_cast<const bf16x8_t*>(src) + b * 4;
@@ -185,7 +196,7 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const void* __restrict
     }
     *reinterpret_cast<i32x4_t*>(codes + b * 32) = out[0];
     *reinterpret_cast<i32x4_t*>(codes + b * 32 + 16) = out[1];
-    scales[b] = (uint8_t)(X + 127);
+    scales[s] = (uint8_t)(X + 127);
   }
 }
 
@@ -334,6 +345,7 @@ hipError_t launch_grouped_gemm_bf16(const GemmProblem& gp, hipStream_t s) {
   a.c_scale = nullptr;
   a.a_scale = nullptr;
   a.w_scale = nullptr;
+  a.a_scale_bytes = a.w_scale_bytes = 0;
   const int grid = device_cu_count();
   const int group_cols = grid / kXcds > 0 ? grid / kXcds : 1;
   SplitWs sp{nullptr, nullptr, nullptr};
@@ -366,10 +378,11 @@ hipError_t launch_grouped_gemm_mx(const GemmProblem& gp, hipStream_t s) {
   a.c_scale = nullptr;
   a.a_scale = nullptr;
   a.w_scale = nullptr;
+  a.a_scale_bytes = a.w_scale_bytes = 0;
   const int grid = device_cu_count();
   const int group_cols = grid / kXcds > 0 ? grid / kXcds : 1;
   if (gp.layer == 0) {
-    // x_perm, W_gate, W_up bf16; Hact MXFP8: R*F codes, then R*F/32 scales
+    // x_perm, W_gate, W_up bf16; Hact MXFP8: R*F codes, then the scales
     a.a = (const __bf16*)gp.a;
     a.w0 = (const __bf16*)gp.w0;
     a.w1 = (const __bf16*)gp.w1;
@@ -380,8 +393,10 @@ hipError_t launch_grouped_gemm_mx(const GemmProblem& gp, hipStream_t s) {
     // Hact and W_down MXFP8 (codes, then scales); Y f32
     a.a = (const __bf16*)gp.a;
     a.a_scale = reinterpret_cast<const uint8_t*>(gp.a) + gp.R * gp.K;
+    a.a_scale_bytes = (uint32_t)mx_scale_bytes(gp.R, gp.K);
     a.w0 = (const __bf16*)gp.w0;
     a.w_scale = reinterpret_cast<const uint8_t*>(gp.w0) + (int64_t)gp.E * gp.N * gp.K;
+    a.w_scale_bytes = (uint32_t)mx_scale_bytes((int64_t)gp.E * gp.N, gp.K);
     a.w1 = nullptr;
     a.c = gp.c;
     grouped_gemm_mx_kernel<<<grid, kGemmThreads, 0, s>>>(a, gp.offsets, gp.G, group_cols);
@@ -390,7 +405,7 @@ hipError_t launch_grouped_gemm_mx(const GemmProblem& gp, hipStream_t s) {
 }
 
 hipError_t launch_mx_quantize(const void* src, int src_bf16, int64_t rows, int cols, void* dst, hipStream_t s) {
-  const int64_t nblk = rows * (cols / 32);
+  const int64_t nblk = mx_scale_bytes(rows, cols);
   if (nblk == 0) return hipSuccess;
   uint8_t* codes = reinterpret_cast<uint8_t*>(dst);
   const int64_t blocks = (nblk + 255) / 256;

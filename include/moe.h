@@ -77,8 +77,15 @@ typedef enum {
  * s, value = e4m3(code) * 2^(s - 127); the scale is 2^X with X =
  * floor(log2 of the block's largest magnitude) - 8 (or s = 0 for an
  * all-zero block), codes are the nearest e4m3 value (ties to even),
- * magnitudes past 448 become 448.  An MXFP8 tensor of rows x cols is ONE
- * buffer: rows*cols codes, then rows*cols/32 scale bytes (row-major). */
+ * magnitudes past 448 become 448.  An MXFP8 tensor of rows x cols (cols a
+ * multiple of 128) is ONE buffer: rows*cols codes (row-major), then the
+ * scale bytes in groups of 32 rows (rows padded to a multiple of 32): the
+ * byte of row r, block b (columns 32b .. 32b+31) sits at
+ *   (r / 32) * cols + (b / 4) * 128 + (r % 32) * 4 + b % 4,
+ * so per group and 128-column quad the 4 bytes of each row lie together.
+ * Buffer size: rows*cols + ceil(rows/32)*32*cols/32 bytes.  No reader
+ * uses the padding rows' bytes; moe_quantize_mxfp8 writes them as 0,
+ * layer 0 leaves them as they are. */
 typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1, MOE_DTYPE_BF16_MXFP8 = 2 } moe_dtype_t;
 
 /* Operation whose workspace moe_workspace_bytes sizes. */
@@ -277,9 +284,10 @@ moe_status_t moe_layer(const moe_problem_t* p, const void* x, const float* logit
 /*
  * MXFP8 quantisation (the format of MOE_DTYPE_BF16_MXFP8) of rows x cols
  * values, blocks of 32 along a row: src [rows, cols] bf16 (src_dtype
- * MOE_DTYPE_BF16) or f32; dst one buffer of rows*cols + rows*cols/32 bytes
- * (codes, then scales).  cols a multiple of 32; src and dst 16-byte
- * aligned.  For W_down, rows = EL*H and cols = F.
+ * MOE_DTYPE_BF16) or f32; dst one MXFP8 buffer of rows*cols +
+ * ceil(rows/32)*32*cols/32 bytes (codes, then scales in the grouped order
+ * above).  cols a multiple of 128 (else MOE_ERR_INVALID_ARGUMENT); src and
+ * dst 16-byte aligned.  For W_down, rows = EL*H and cols = F.
  */
 moe_status_t moe_quantize_mxfp8(int64_t rows, int32_t cols, int32_t src_dtype, const void* src, void* dst,
                                 void* stream);

@@ -16,6 +16,7 @@
 namespace moe {
 
 constexpr int kCombineThreads = 256;
+constexpr int kCombineUnroll = 4;
 
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* __restrict__ y,
                                                                   const float* __restrict__ topk_w,
@@ -30,9 +31,37 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
       w[threadIdx.x] = topk_w[t * k + threadIdx.x];
     }
     __syncthreads();
-    for (int q = threadIdx.x; q < groups; q += kCombineThreads) {
-      const float4 o = combine_group(y, w, rows, k, H, (int64_t)q * 4);
-      store_out(ep, t * H + (int64_t)q * 4, o);
+    // kCombineUnroll column groups per thread at a time: each slot's loads
+    // for all of them are issued before any is used (the per-element
+    // arithmetic is combine_group's: from zero, slots in order, fmaf)
+    for (int q0 = threadIdx.x; q0 < groups; q0 += kCombineThreads * kCombineUnroll) {
+      float4 acc[kCombineUnroll];
+#pragma unroll
+      for (int u = 0; u < kCombineUnroll; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int j = 0; j < k; ++j) {
+        const int32_t row = rows[j];
+        if (row < 0) continue;
+        const float wj = w[j];
+        const float* yr = y + (int64_t)row * H;
+        float4 v[kCombineUnroll];
+#pragma unroll
+        for (int u = 0; u < kCombineUnroll; ++u) {
+          const int q = q0 + u * kCombineThreads;
+          v[u] = q < groups ? *reinterpret_cast<const float4*>(yr + (int64_t)q * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < kCombineUnroll; ++u) {
+          acc[u].x = fmaf(wj, v[u].x, acc[u].x);
+          acc[u].y = fmaf(wj, v[u].y, acc[u].y);
+          acc[u].z = fmaf(wj, v[u].z, acc[u].z);
+          acc[u].w = fmaf(wj, v[u].w, acc[u].w);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kCombineUnroll; ++u) {
+        const int q = q0 + u * kCombineThreads;
+        if (q < groups) store_out(ep, t * H + (int64_t)q * 4, acc[u]);
+      }
     }
     __syncthreads();
   }

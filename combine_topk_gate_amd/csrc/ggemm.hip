@@ -62,6 +62,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(Bf16Gem
   __shared__ TileLds tl;
   const int NT = (args.N + (LAYER == 0 ? kL0Cols : kL1Cols) - 1) / (LAYER == 0 ? kL0Cols : kL1Cols);
   const int T = build_tile_table(offsets, G, kTileRows, tl) * NT;
+  const int64_t rtb = (int64_t)kTileRows * args.K * 2;  // bytes of a tile's operand panel (bf16)
   const int grid = gridDim.x;
   const int r = T % grid;
   if constexpr (LAYER == 1 && !OUT8) {
@@ -78,11 +79,11 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(Bf16Gem
       const int entries = tail0 + r * s;
       for (int v = xcd_slot(blockIdx.x, grid); v < entries; v += grid) {
         if (v < tail0) {
-          const TileCoord c = tile_coord(v, G, NT, kTileRows, group_cols, tl);
+          const TileCoord c = tile_coord(v, G, NT, kTileRows, group_cols, rtb, tl);
           bf16_gemm_row_tile<LAYER>(args, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], c.m0, c.nt, lds);
         } else {
           const int u = v - tail0, jj = u / s, ck = u - jj * s;
-          const TileCoord c = tile_coord(tail0 + jj, G, NT, kTileRows, group_cols, tl);
+          const TileCoord c = tile_coord(tail0 + jj, G, NT, kTileRows, group_cols, rtb, tl);
           if (ck == 0 && threadIdx.x == 0) {
             int32_t* d = split.desc + 4 * jj;
             d[0] = tl.seg_start[c.g];
@@ -102,11 +103,11 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(Bf16Gem
   const int entries = T + half;
   for (int v = xcd_slot(blockIdx.x, grid); v < entries; v += grid) {
     if (v < T - half) {
-      const TileCoord c = tile_coord(v, G, NT, kTileRows, group_cols, tl);
+      const TileCoord c = tile_coord(v, G, NT, kTileRows, group_cols, rtb, tl);
       bf16_gemm_row_tile<LAYER, false, OUT8>(args, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], c.m0, c.nt, lds);
     } else {
       const int j = v - (T - half);
-      const TileCoord c = tile_coord(T - half + j / 2, G, NT, kTileRows, group_cols, tl);
+      const TileCoord c = tile_coord(T - half + j / 2, G, NT, kTileRows, group_cols, rtb, tl);
       const int m0 = c.m0 + (j & 1) * (kTileRows / 2);
       if (m0 < tl.seg_rows[c.g])
         bf16_gemm_tile<LAYER, false, kTileRows / 2, false, OUT8>(args, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], m0,
@@ -126,20 +127,21 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_mx_kernel(Bf16GemmA
   __shared__ TileLds tl;
   const int NT = (args.N + kL1Cols - 1) / kL1Cols;
   const int T = build_tile_table(offsets, G, kTileRows, tl) * NT;
+  const int64_t rtb = (int64_t)kTileRows * args.K;  // bytes of a tile's operand panel (fp8 codes)
   const int grid = gridDim.x;
   const int r = T % grid;
   const int half = (r > 0 && 2 * r <= grid && T > grid) ? r : 0;
   const int entries = T + half;
   for (int v = xcd_slot(blockIdx.x, grid); v < entries; v += grid) {
     if (v < T - half) {
-      const TileCoord c = tile_coord(v, G, NT, kTileRows, group_cols, tl);
+      const TileCoord c = tile_coord(v, G, NT, kTileRows, group_cols, rtb, tl);
       if (tl.seg_rows[c.g] <= kTileRows / 2)
         mx_gemm_tile<kTileRows / 2>(args, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], c.m0, c.nt, lds);
       else
         mx_gemm_tile<kTileRows>(args, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], c.m0, c.nt, lds);
     } else {
       const int j = v - (T - half);
-      const TileCoord c = tile_coord(T - half + j / 2, G, NT, kTileRows, group_cols, tl);
+      const TileCoord c = tile_coord(T - half + j / 2, G, NT, kTileRows, group_cols, rtb, tl);
       const int m0 = c.m0 + (j & 1) * (kTileRows / 2);
       if (m0 < tl.seg_rows[c.g]) mx_gemm_tile<kTileRows / 2>(args, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], m0, c.nt, lds);
     }
@@ -252,7 +254,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(const float* __re
   const int total = build_tile_table(offsets, G, kF32Rows, tl) * NT;
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   for (int v = blockIdx.x; v < total; v += gridDim.x) {
-    const TileCoord c = tile_coord(v, G, NT, kF32Rows, 1, tl);
+    const TileCoord c = tile_coord(v, G, NT, kF32Rows, 1, 0, tl);
     const int e = c.g % E, s0 = tl.seg_start[c.g], nrows = tl.seg_rows[c.g];
     const int col0 = c.nt * cols;
     const int64_t ebase = (int64_t)e * N * K;

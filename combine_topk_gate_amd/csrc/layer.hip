@@ -228,7 +228,7 @@ __global__ __launch_bounds__(kGemmThreads) void fused_layer_kernel(FusedArgs a) 
     const int v = (i / run) * (nq * run) + q * run + (i % run);
     if (v >= total) return;
     if (v < T0) {
-      const TileCoord c = tile_coord(v, a.G, nt0, kTileRows, group_cols, tl);
+      const TileCoord c = tile_coord(v, a.G, nt0, kTileRows, group_cols, (int64_t)kTileRows * a.H * 2, tl);
       ga.a = reinterpret_cast<const __bf16*>(a.x);
       ga.w0 = reinterpret_cast<const __bf16*>(a.w_gate);
       ga.w1 = reinterpret_cast<const __bf16*>(a.w_up);
@@ -261,7 +261,7 @@ __global__ __launch_bounds__(kGemmThreads) void fused_layer_kernel(FusedArgs a) 
       }
     }
     if (is_tile) {
-      const TileCoord c = tile_coord(u, a.G, chunk_width(chunk), kTileRows, group_cols, tl);
+      const TileCoord c = tile_coord(u, a.G, chunk_width(chunk), kTileRows, group_cols, (int64_t)kTileRows * a.F * 2, tl);
       if (!block_wait(l0done + c.mt, nt0, a.status, limit, &lds_word)) return;
       ga.a = reinterpret_cast<const __bf16*>(a.hact);
       ga.w0 = reinterpret_cast<const __bf16*>(a.w_down);

@@ -10,8 +10,8 @@
 // A segment of n rows has ceil(n / rows) row tiles ("M-tiles"); mt_start[g]
 // is the exclusive prefix of the M-tile counts.  With NT column tiles, the
 // tiles of segment g occupy [mt_start[g] * NT, mt_start[g+1] * NT) of the
-// queue.  Inside a segment: column groups of gn tiles, and inside a group
-// the row tiles fastest.  A persistent workgroup walks virtual slots
+// queue, in blocks of row tiles and column groups (tile_coord).  A
+// persistent workgroup walks virtual slots
 // it*grid + v, and v is chosen so that the workgroups of one XCD (hardware
 // ids w, w+8, ... are dispatched round-robin over the 8 XCDs) own a
 // contiguous run of slots: concurrently running tiles on one XCD then share
@@ -81,20 +81,50 @@ struct TileCoord {
   int mt;  // global M-tile index
 };
 
+// What the last-level cache (256 MB on MI355X, shared by the XCDs) keeps
+// while a segment's tiles go by: its token rows up to kResidentRowBytes,
+// its weight panels up to kResidentWeightBytes (the weights are read in a
+// second pass over them, the token rows over and over).
+constexpr int64_t kResidentRowBytes = 64ll << 20;
+constexpr int64_t kResidentWeightBytes = 128ll << 20;
+
 // Tile v of a queue over NT column tiles (per segment mt_g * NT tiles).
-__device__ inline TileCoord tile_coord(int v, int G, int NT, int rows, int group_cols, const TileLds& t) {
+// panel_bytes is the bytes of one tile's operand panel over the whole
+// reduction (tokens of a row tile, weights of a column tile: both 256 rows).
+// Inside a segment: column groups of group_cols / mt tiles with the row
+// tiles fastest, so each weight panel is read once while the segment's
+// token rows are re-read from the cache.  A segment of more than
+// group_cols / 4 row tiles whose token rows are too big for the cache, or
+// whose weight panels are small enough to be read twice from it, is cut
+// into nb = ceil(mt / (group_cols / 4)) blocks of row tiles of nearly equal
+// height, each ordered as a segment of its own (8 x 4 tiles per column
+// group for 32 slots, against one column of every row tile).  Block b holds
+// rows [b mt / nb, (b + 1) mt / nb), i.e. queue entries [row0 NT, row1 NT).
+__device__ inline TileCoord tile_coord(int v, int G, int NT, int rows, int group_cols, int64_t panel_bytes,
+                                       const TileLds& t) {
   const int g = find_segment(v, G, NT, t.mt_start);
   const int l = v - t.mt_start[g] * NT;
   const int mt = t.mt_start[g + 1] - t.mt_start[g];
-  int gn = group_cols / (mt > 0 ? mt : 1);
+  const int rbmax = group_cols / 4 > 0 ? group_cols / 4 : 1;
+  const bool block = panel_bytes > 0 && mt > rbmax &&
+                     ((int64_t)mt * panel_bytes > kResidentRowBytes || (int64_t)NT * panel_bytes <= kResidentWeightBytes);
+  const int nb = block ? (mt + rbmax - 1) / rbmax : 1;
+  const int r = l / NT;  // a row of l's block
+  auto row_of = [&](int bb) { return (int)(((int64_t)bb * mt) / nb); };  // first row of block bb
+  int b = (int)(((int64_t)r * nb) / mt);
+  if (b > nb - 1) b = nb - 1;
+  if (row_of(b + 1) <= r) ++b;
+  const int r0 = row_of(b), rb = row_of(b + 1) - r0;
+  const int lb = l - r0 * NT;
+  int gn = group_cols / rb;
   if (gn < 1) gn = 1;
-  const int span = mt * gn;
-  const int grp = l / span, rem = l - grp * span;
+  const int span = rb * gn;
+  const int grp = lb / span, rem = lb - grp * span;
   TileCoord c;
   c.g = g;
-  const int mi = rem % mt;
+  const int mi = r0 + rem % rb;
   c.m0 = mi * rows;
-  c.nt = grp * gn + rem / mt;
+  c.nt = grp * gn + rem / rb;
   c.mt = t.mt_start[g] + mi;
   return c;
 }

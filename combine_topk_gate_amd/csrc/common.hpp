@@ -61,23 +61,17 @@ __host__ __device__ __forceinline__ int64_t mx_scale_bytes(int64_t rows, int64_t
   return (rows + 31) / 32 * 32 * (cols / 32);
 }
 
-// e4m3 code of v (already divided by the block scale, |v| < 512): round to
-// nearest, ties to even, magnitudes past 448 give 448 (0x7E); sign of v.
-// Normal range (|v| >= 2^-6): v = 2^E (1 + m/8), code (E + 7) * 8 + m, where
-// a mantissa rounded up to 8 carries into the exponent by itself;
-// subnormals are multiples of 2^-9 (code = the multiple, 8 = 2^-6).
-__device__ __forceinline__ uint32_t e4m3_code(float v) {
-  const uint32_t bits = __builtin_bit_cast(uint32_t, v);
-  const uint32_t sign = (bits >> 24) & 0x80u;
-  const float a = __builtin_bit_cast(float, bits & 0x7FFFFFFFu);
-  int code;
-  if (a >= 0x1p-6f) {
-    const int E = (int)((bits >> 23) & 0xFF) - 127;
-    code = (E + 7) * 8 + (int)rintf((ldexpf(a, -E) - 1.0f) * 8.0f);
-  } else {
-    code = (int)rintf(a * 512.0f);
-  }
-  return sign | (uint32_t)(code < 126 ? code : 126);
+// e4m3 codes of four values already divided by the block scale (|v| <
+// 512), packed little-endian: round to nearest, ties to even, magnitudes
+// past 448 give 448 (0x7E), sign kept.  The values are first clamped to
+// [-448, 448], so the hardware conversion (OCP e4m3 on gfx950, correctly
+// rounded in the default round-to-nearest-even mode) never overflows;
+// inside that range its rounding is the format's.
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+  auto sat = [](float v) { return __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f); };
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(a), sat(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(c), sat(d), w, true);
+  return (uint32_t)w;
 }
 
 // Top-k weighted reduction of one 4-wide column group, shared by the

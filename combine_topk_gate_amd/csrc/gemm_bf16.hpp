@@ -87,7 +87,7 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 // fixed order.  Otherwise k0 = 0, k1 = K / kBK (the whole reduction).
 //
 // OUT8 (layer 0): Hact is written as MXFP8 instead of bf16: e4m3 codes and,
-// per 32 columns of a token row, one scale byte (see mx_scale / e4m3_code).
+// per 32 columns of a token row, one scale byte (see mx_scale / e4m3_pack4).
 template <int LAYER, bool GATHER = false, int TM = kTileRows, bool PARTIAL = false, bool OUT8 = false>
 __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int seg_start, int seg_rows, int m0,
                                                int nt, char* __restrict__ lds, int k0 = 0, int k1 = -1,
@@ -457,12 +457,9 @@ __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int
       const int X = mx_scale(amax);
       i32x4_t out[2];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w |= e4m3_code(ldexpf(v[j][i], -X)) << (8 * i);
-        out[j / 4][j % 4] = (int)w;
-      }
+      for (int j = 0; j < 8; ++j)
+        out[j / 4][j % 4] = (int)e4m3_pack4(ldexpf(v[j][0], -X), ldexpf(v[j][1], -X), ldexpf(v[j][2], -X),
+                                            ldexpf(v[j][3], -X));
       const int trow = m0 + t;
       if (trow < seg_rows && f < N) {
         uint8_t* dst = hact + (int64_t)(seg_start + trow) * N + f;

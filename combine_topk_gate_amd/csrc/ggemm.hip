@@ -190,12 +190,9 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const void* __restrict
     const int X = mx_scale(amax);
     i32x4_t out[2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t w = 0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) w |= e4m3_code(ldexpf(v[4 * i + j], -X)) << (8 * j);
-      out[i / 4][i % 4] = (int)w;
-    }
+    for (int i = 0; i < 8; ++i)
+      out[i / 4][i % 4] = (int)e4m3_pack4(ldexpf(v[4 * i], -X), ldexpf(v[4 * i + 1], -X), ldexpf(v[4 * i + 2], -X),
+                                          ldexpf(v[4 * i + 3], -X));
     *reinterpret_cast<i32x4_t*>(codes + b * 32) = out[0];
     *reinterpret_cast<i32x4_t*>(codes + b * 32 + 16) = out[1];
     scales[s] = (uint8_t)(X + 127);

@@ -215,6 +215,9 @@ EDGE = {
     "local_one_expert_f32": dict(M=90, H=64, F=128, E=8, k=3, dtype="f32", base=5, local=1),
     "local_none_routed": dict(M=64, H=128, F=128, E=8, k=2, base=6, local=2,
                               bias=[0, 0, 0, 0, 0, 0, -60, -60]),
+    # segments of 27 and 9 row tiles: the tile order cuts them into row
+    # blocks of uneven height (6/7 rows); every output row still computed once
+    "tall_segments": dict(M=9000, H=256, F=512, E=2, k=1, bias=[1, 0]),
 }
 SPLIT_EDGES = ["split_single_round", "split_empty_experts"]
 

@@ -38,8 +38,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="mixtral")
     ap.add_argument("--mode", choices=("chain", "layer"), default="layer",
                     help="layer: moe_layer with the library's per-shape choice; chain: moe_layer forced unfused")
@@ -130,7 +130,14 @@ def cpu_baseline(cfg, d, target_s):
     # FFN work only for the pairs whose expert is held
     pairs = int((r["flat_to_sorted"].reshape(cfg.M, cfg.k)[toks] >= 0).sum())
     flops = flop_pair * pairs
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "cpu": model,
             "sample": f"{len(toks)} of {cfg.M} tokens ({pairs} held routed rows, seeded), full routing; "
                       f"{dt:.1f} s fp64 on the host; per-token work is exactly linear, so the full layer "
                       f"would take {dt * cfg.M / len(toks):.0f} s"}
@@ -276,7 +283,7 @@ def main():
 
     # (1) the step: one moe_layer call (the library's per-shape choice of the
     #     fused kernel or the chain), timed as a whole
-    ms_step, _ = time_steps(step_layer, 2, args.warmup, args.steps)
+    ms_step, per_layer = time_steps(step_layer, 2, args.warmup, args.steps)
     # (2) the same layer as the chain of C-ABI calls, with an event between
     #     calls: per-step times and the dominant kernel's live duration
     ms_chain, per = time_steps(step_chain, 6, args.warmup, args.steps)
@@ -311,10 +318,13 @@ def main():
                       "experts_held": cfg.EL, "routed_rows_held": Rk,
                       "layer_call": "fused" if (args.mode == "layer" and movers >= 0 and cfg.dtype == "bf16")
                       else "chain", "n_mover": movers},
-           "layer_us": ms_step * 1e3, "chain_us": ms_chain * 1e3}
+           "layer_us": ms_step * 1e3, "chain_us": ms_chain * 1e3,
+           "layer_us_p10_p50_p90": [float(np.percentile(per_layer[:, 0], q)) for q in (10, 50, 90)]}
     mean = per.mean(axis=0)
     names = ["route", "dispatch", "gemm_l0", "gemm_l1", "combine"]
     res["step_us"] = {n: float(v) for n, v in zip(names, mean)}
+    res["step_us_p10_p50_p90"] = {n: [float(np.percentile(per[:, i], q)) for q in (10, 50, 90)]
+                                  for i, n in enumerate(names)}
     t_gemm = (mean[2] + mean[3]) * 1e-6
     peak = PEAK_F32_TFLOPS if cfg.dtype == "f32" else PEAK_BF16_TFLOPS
     res["grouped_gemm_tflops"] = flops / t_gemm / 1e12

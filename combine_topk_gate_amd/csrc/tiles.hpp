@@ -108,14 +108,18 @@ __device__ inline TileCoord tile_coord(int v, int G, int NT, int rows, int group
   const int rbmax = group_cols / 4 > 0 ? group_cols / 4 : 1;
   const bool block = panel_bytes > 0 && mt > rbmax &&
                      ((int64_t)mt * panel_bytes > kResidentRowBytes || (int64_t)NT * panel_bytes <= kResidentWeightBytes);
-  const int nb = block ? (mt + rbmax - 1) / rbmax : 1;
-  const int r = l / NT;  // a row of l's block
-  auto row_of = [&](int bb) { return (int)(((int64_t)bb * mt) / nb); };  // first row of block bb
-  int b = (int)(((int64_t)r * nb) / mt);
-  if (b > nb - 1) b = nb - 1;
-  if (row_of(b + 1) <= r) ++b;
-  const int r0 = row_of(b), rb = row_of(b + 1) - r0;
-  const int lb = l - r0 * NT;
+  int r0 = 0, rb = mt, lb = l;
+  if (block) {
+    const int nb = (mt + rbmax - 1) / rbmax;
+    auto row_of = [&](int bb) { return (int)(((int64_t)bb * mt) / nb); };  // first row of block bb
+    const int r = l / NT;  // a row of l's block
+    int b = (int)(((int64_t)r * nb) / mt);
+    if (b > nb - 1) b = nb - 1;
+    if (row_of(b + 1) <= r) ++b;
+    r0 = row_of(b);
+    rb = row_of(b + 1) - r0;
+    lb = l - r0 * NT;
+  }
   int gn = group_cols / rb;
   if (gn < 1) gn = 1;
   const int span = rb * gn;

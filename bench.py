@@ -335,7 +335,7 @@ def main():
         res["gemm_l1_mxfp8_pct_peak"] = 100.0 * 2.0 * Rk * H * F / (mean[3] * 1e-6) / 1e12 / PEAK_FP8_TFLOPS
     else:
         res["grouped_gemm_pct_peak"] = 100.0 * res["grouped_gemm_tflops"] / peak
-    eb = 2 if cfg.dtype == "bf16" else 4
+    eb = 4 if cfg.dtype == "f32" else 2  # bytes of an x / X_perm element
     # token rows read (those with a held pair), rows written, the index list
     disp_bytes = Tk * H * eb + Rk * H * eb + R * 4
     comb_bytes = Rk * H * 4 + M * H * 4 + M * k * 8

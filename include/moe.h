@@ -303,8 +303,10 @@ moe_status_t moe_layer_ex(const moe_problem_t* p, const void* x, const float* lo
 /* The plan the profiled split table picks for this problem (what moe_layer
  * does when opts->n_mover < 0): the number of dedicated combine workgroups
  * of the fused kernel (0: the combine shares the work queue), or -1 when the
- * layer runs as the kernel chain (f32 layers, and shapes where profiling
- * found the chain faster) or the problem is invalid. */
+ * layer runs as the kernel chain (f32 and MXFP8 layers, shapes where
+ * profiling found the chain faster, and shapes the table does not list:
+ * on MI355X the chain was faster on every shape measured) or the problem
+ * is invalid. */
 int32_t moe_layer_default_movers(const moe_problem_t* p);
 
 /* Synchronises `stream` and returns the device status the last moe_layer

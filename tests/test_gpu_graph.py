@@ -35,7 +35,9 @@ def test_layer_graph_replays_equal_eager(dtype, fused):
               (g["x"].clone(), g["logits"].clone())]
 
     def call(out):
-        moe.moe_layer(p, g["x"], g["logits"], None, g["w_gate"], g["w_up"], g["w_down"], out, ws, fused=fused)
+        # fused: the fused kernel with the combine in the shared queue; else the chain
+        moe.moe_layer(p, g["x"], g["logits"], None, g["w_gate"], g["w_up"], g["w_down"], out, ws,
+                      fused=fused, n_mover=0 if fused else -1)
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())

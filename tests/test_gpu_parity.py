@@ -218,6 +218,10 @@ EDGE = {
     # segments of 27 and 9 row tiles: the tile order cuts them into row
     # blocks of uneven height (6/7 rows); every output row still computed once
     "tall_segments": dict(M=9000, H=256, F=512, E=2, k=1, bias=[1, 0]),
+    # the most segments a call may rank: 16 source blocks x 64 experts = 1024
+    "max_segments": dict(M=2048, H=64, F=128, E=64, k=2, S=16),
+    # ... and with held experts: 15 blocks x 68 held + the dropped pairs' = 1021
+    "max_segments_held": dict(M=1920, H=64, F=128, E=128, k=4, S=15, base=30, local=68),
 }
 SPLIT_EDGES = ["split_single_round", "split_empty_experts"]
 

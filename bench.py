@@ -193,7 +193,7 @@ def main():
         copy_calibration()
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "the MoE layer benchmark runs on one GPU only; --gpus must be 1", "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
 

@@ -72,15 +72,19 @@ __global__ __launch_bounds__(kMaxSegments) void seg_scan_kernel(int G, int Gr, i
   __shared__ int tot[kMaxSegments];
   int gp = 1;
   while (gp < G) gp <<= 1;
-  const int P = kMaxSegments / gp;  // threads per segment
+  // slices per segment: as many as fit, but no more than there are blocks
+  // (the prefix over slices below is serial in P)
+  int P = kMaxSegments / gp;
+  if (P > blocks) P = blocks > 0 ? blocks : 1;
   const int g = threadIdx.x % gp, p = threadIdx.x / gp;
+  const bool active = p < P;
   const int L = (blocks + P - 1) / P;
   const int b0 = p * L, b1 = min(blocks, b0 + L);
   int sum = 0;
-  if (g < G)
+  if (active && g < G)
 #pragma unroll 8
     for (int b = b0; b < b1; ++b) sum += block_hist[(int64_t)b * G + g];
-  part[threadIdx.x] = sum;
+  if (active) part[threadIdx.x] = sum;
   __syncthreads();
   // exclusive prefix over the P slices of each segment, and the segment total
   if (threadIdx.x < gp) {
@@ -107,7 +111,7 @@ __global__ __launch_bounds__(kMaxSegments) void seg_scan_kernel(int G, int Gr, i
   if (G == Gr && threadIdx.x == 0) offsets[Gr] = (int)R;
   __syncthreads();
   // block_hist[b][g] <- offsets[g] + pairs of segment g in blocks before b
-  if (g < G) {
+  if (active && g < G) {
     int run = s[g] - tot[g] + part[threadIdx.x];  // offsets[g] + blocks before this slice
 #pragma unroll 8
     for (int b = b0; b < b1; ++b) {

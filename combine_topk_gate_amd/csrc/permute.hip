@@ -210,8 +210,8 @@ hipError_t launch_permute(const PermutePlan& pl, const int32_t* topk_idx, const 
 // Each token row is read once and written to its k sorted positions,
 // 16 bytes per lane; a block walks whole rows (two at a time, so each lane
 // has several loads in flight) and the writes of one row are contiguous.
-// X_perm is written with non-temporal stores: it is consumed by the next
-// kernel from HBM, so keeping it out of the caches leaves them to the reads.
+// X_perm is written with ordinary stores (measured on MI355X: 33.7 us for
+// Mixtral's 201 MB against 39.7 us with non-temporal stores).
 constexpr int kCopyThreads = 256;
 constexpr int kCopyRows = 2;
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(kCopyThreads) void dispatch_copy_kernel(const u32x4
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const int c = c0 + u * kCopyThreads;
-            if (c < C) __builtin_nontemporal_store(v[r][u], d + c);
+            if (c < C) d[c] = v[r][u];
           }
         }
       }

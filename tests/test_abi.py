@@ -152,3 +152,26 @@ def test_workspace_sizes_cover_intermediates(lib):
         assert moe.moe_workspace_bytes(p, moe.MOE_OP_DISPATCH) >= 4 * S * E
     p32 = moe.problem(256, 256, 512, 8, 2, 1, "f32")
     assert moe.moe_workspace_bytes(p32, moe.MOE_OP_GROUPED_GEMM) == 0
+
+
+def test_mxfp8_quantiser_rejects_bad_arguments(lib):
+    fake = ctypes.c_void_p(1 << 20)
+    lib.moe_quantize_mxfp8.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p]
+    inval = moe.MOE_ERR_INVALID_ARGUMENT
+    # columns must be a whole number of 128-column quads (the scale layout's unit)
+    for cols in (0, 32, 96, 200, 384 + 32):
+        assert lib.moe_quantize_mxfp8(4, cols, moe.MOE_DTYPE_BF16, fake, fake, None) == inval, cols
+    assert lib.moe_quantize_mxfp8(-1, 128, moe.MOE_DTYPE_BF16, fake, fake, None) == inval
+    assert lib.moe_quantize_mxfp8(4, 128, moe.MOE_DTYPE_BF16_MXFP8, fake, fake, None) == inval  # src dtype
+    assert lib.moe_quantize_mxfp8(4, 128, moe.MOE_DTYPE_BF16, None, fake, None) == inval
+    assert lib.moe_quantize_mxfp8(4, 128, moe.MOE_DTYPE_F32, fake, ctypes.c_void_p((1 << 20) + 8), None) == inval
+    assert lib.moe_quantize_mxfp8(0, 128, moe.MOE_DTYPE_BF16, None, None, None) == moe.MOE_OK  # nothing to do
+
+
+def test_mx_buffer_size_matches_the_layout():
+    # codes, then one scale byte per 32 values with rows padded to 32
+    assert moe.mx_bytes(1, 128) == 128 + 32 * 4
+    assert moe.mx_bytes(32, 256) == 32 * 256 + 32 * 8
+    assert moe.mx_bytes(33, 256) == 33 * 256 + 64 * 8
+    assert moe.mx_bytes(0, 128) == 0

@@ -1,9 +1,12 @@
-"""bench.py's command-line contract that holds without a GPU: it runs on
-one GPU only and says so for --gpus N > 1."""
+"""bench.py's command-line contract: on any machine it refuses --gpus N > 1
+with a message; on a GPU it prints one JSON line with the keys the
+benchmark contract names (a short run of a small workload)."""
 import json
 import os
 import subprocess
 import sys
+
+import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -14,3 +17,20 @@ def test_more_than_one_gpu_is_refused_with_a_message():
     assert r.returncode == 2
     msg = json.loads(r.stdout.strip().splitlines()[-1])
     assert msg["n_gpus"] == 2 and "one GPU" in msg["error"]
+
+
+@pytest.mark.gpu
+def test_bench_prints_one_json_line_with_the_contract_keys():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--config", "qwen2", "--steps", "2",
+                        "--warmup", "1", "--no-cpu-baseline", "--no-dense-ref"], capture_output=True, text=True,
+                       timeout=600)
+    assert r.returncode == 0, r.stderr[-2000:]
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+                "scaling", "vs_baseline", "dtype", "data", "config", "roofline"):
+        assert key in d, key
+    assert d["n_gpus"] == 1 and d["steps"] == 2 and d["warmup"] == 1 and d["value"] > 0
+    rf = d["roofline"]
+    assert rf["bound"] == "mfma" and rf["unit"] == "TFLOP/s" and 0 < rf["frac"] < 1
+    assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-9
+    assert d["config"]["workload"].startswith("qwen2")

@@ -1,7 +1,11 @@
 // C ABI of the library: host-side argument checks, workspace carving and
 // kernel launches.  Every entry point only enqueues work on the caller's
 // stream; none synchronises (except moe_debug_device_status, a test hook).
+#include <math.h>
+#include <stdlib.h>
 #include <string.h>
+
+#include <vector>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -78,6 +82,90 @@ moe_status_t epilogue_of(const moe_problem_t* p, const moe_epilogue_t* epi, void
 
 moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// ------------------------------------------------------ debug validation --
+// MOE_DEBUG_VALIDATE=1 in the environment: before launching anything, each
+// entry point copies the device-resident inputs it trusts to the host
+// (synchronising the stream) and checks them: logits finite, topk_idx in
+// [0, E), src_block in [0, S), offsets starting at 0, non-decreasing and
+// ending at most at R, flat_to_sorted in [-1, R).  A failed check returns
+// MOE_ERR_INVALID_ARGUMENT and launches nothing.  Host memory only; for
+// debugging, not for timed runs.
+bool debug_validate() {
+  const char* v = getenv("MOE_DEBUG_VALIDATE");
+  return v && v[0] == '1' && v[1] == 0;
+}
+
+template <typename T>
+bool fetch(std::vector<T>& h, const T* d, int64_t n, hipStream_t s) {
+  h.resize(n > 0 ? (size_t)n : 0);
+  if (n <= 0) return true;
+  if (hipMemcpyAsync(h.data(), d, (size_t)n * sizeof(T), hipMemcpyDeviceToHost, s) != hipSuccess) return false;
+  return hipStreamSynchronize(s) == hipSuccess;
+}
+
+moe_status_t check_range(const int32_t* d, int64_t n, int32_t lo, int32_t hi, hipStream_t s) {
+  std::vector<int32_t> h;
+  if (!fetch(h, d, n, s)) return MOE_ERR_HIP;
+  for (int32_t v : h)
+    if (v < lo || v >= hi) return MOE_ERR_INVALID_ARGUMENT;
+  return MOE_OK;
+}
+
+moe_status_t validate_logits(const moe_problem_t* p, const float* logits, hipStream_t s) {
+  std::vector<float> h;
+  if (!fetch(h, logits, p->num_tokens * (int64_t)p->num_experts, s)) return MOE_ERR_HIP;
+  for (float v : h)
+    if (!isfinite(v)) return MOE_ERR_INVALID_ARGUMENT;
+  return MOE_OK;
+}
+
+moe_status_t validate_routing(const moe_problem_t* p, const int32_t* topk_idx, const int32_t* src_block,
+                              hipStream_t s) {
+  moe_status_t st = check_range(topk_idx, p->num_tokens * (int64_t)p->topk, 0, p->num_experts, s);
+  if (st == MOE_OK && p->num_src_blocks > 1) st = check_range(src_block, p->num_tokens, 0, p->num_src_blocks, s);
+  return st;
+}
+
+moe_status_t validate_offsets(const moe_problem_t* p, const int32_t* offsets, hipStream_t s) {
+  std::vector<int32_t> h;
+  const int G = segments(p);
+  if (!fetch(h, offsets, G + 1, s)) return MOE_ERR_HIP;
+  if (h[0] != 0) return MOE_ERR_INVALID_ARGUMENT;
+  for (int g = 0; g < G; ++g)
+    if (h[g + 1] < h[g]) return MOE_ERR_INVALID_ARGUMENT;
+  if ((int64_t)h[G] > p->num_tokens * p->topk) return MOE_ERR_INVALID_ARGUMENT;
+  return MOE_OK;
+}
+
+// ------------------------------------------------------------ dispatch ---
+// Argument checks of moe_dispatch and its allocation-free variant.
+moe_status_t check_dispatch(const moe_problem_t* p, const void* x, const int32_t* topk_idx,
+                            const int32_t* src_block, const int32_t* counts, const int32_t* offsets,
+                            const int32_t* sorted_to_flat, const int32_t* flat_to_sorted, const void* x_perm) {
+  moe_status_t st = check_problem(p);
+  if (st != MOE_OK) return st;
+  if (!counts || !offsets) return MOE_ERR_INVALID_ARGUMENT;
+  if (p->num_src_blocks > 1 && !src_block && p->num_tokens > 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (p->num_tokens > 0) {
+    if (!x || !topk_idx || !sorted_to_flat || !flat_to_sorted || !x_perm) return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned(x, 16) || !aligned(x_perm, 16)) return MOE_ERR_INVALID_ARGUMENT;
+  }
+  return MOE_OK;
+}
+
+// Bookkeeping and copy of the dispatch with the scratch `ws` (already sized).
+moe_status_t dispatch_launch(const moe_problem_t* p, const void* x, const int32_t* topk_idx,
+                             const int32_t* src_block, int32_t* counts, int32_t* offsets, int32_t* sorted_to_flat,
+                             int32_t* flat_to_sorted, void* x_perm, void* ws, hipStream_t s) {
+  if (debug_validate() && p->num_tokens > 0) {
+    const moe_status_t st = validate_routing(p, topk_idx, src_block, s);
+    if (st != MOE_OK) return st;
+  }
+  return hip_status(launch_dispatch(plan_of(p), topk_idx, p->num_src_blocks > 1 ? src_block : nullptr, counts,
+                                    offsets, sorted_to_flat, flat_to_sorted, x, (int64_t)p->hidden * elem_bytes(p),
+                                    x_perm, (int32_t*)ws, s));
+}
+
 // Workspace of the whole layer, carved in this order (each region 256-B aligned).
 struct LayerWs {
   size_t status, topk_idx, topk_w, counts, offsets, s2f, f2s, perm, x_perm, hact, y, fused, gemm, total;
@@ -147,6 +235,10 @@ moe_status_t moe_route(const moe_problem_t* p, const float* logits, int32_t* top
   if (p->num_tokens == 0) return MOE_OK;
   if (!logits || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned(logits, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4)) return MOE_ERR_INVALID_ARGUMENT;
+  if (debug_validate()) {
+    st = validate_logits(p, logits, (hipStream_t)stream);
+    if (st != MOE_OK) return st;
+  }
   return hip_status(launch_route(logits, p->num_tokens, p->num_experts, p->topk, topk_idx, topk_w,
                                  (hipStream_t)stream));
 }
@@ -154,23 +246,11 @@ moe_status_t moe_route(const moe_problem_t* p, const float* logits, int32_t* top
 moe_status_t moe_dispatch(const moe_problem_t* p, const void* x, const int32_t* topk_idx, const int32_t* src_block,
                           int32_t* counts, int32_t* offsets, int32_t* sorted_to_flat, int32_t* flat_to_sorted,
                           void* x_perm, void* ws, size_t ws_bytes, void* stream) {
-  moe_status_t st = check_problem(p);
+  moe_status_t st = check_dispatch(p, x, topk_idx, src_block, counts, offsets, sorted_to_flat, flat_to_sorted, x_perm);
   if (st != MOE_OK) return st;
-  if (!counts || !offsets) return MOE_ERR_INVALID_ARGUMENT;
-  if (p->num_src_blocks > 1 && !src_block && p->num_tokens > 0) return MOE_ERR_INVALID_ARGUMENT;
-  const int64_t M = p->num_tokens;
-  if (M > 0) {
-    if (!x || !topk_idx || !sorted_to_flat || !flat_to_sorted || !x_perm) return MOE_ERR_INVALID_ARGUMENT;
-    if (!aligned(x, 16) || !aligned(x_perm, 16)) return MOE_ERR_INVALID_ARGUMENT;
-  }
-  const PermutePlan pl = plan_of(p);
-  if (ws_bytes < permute_ws_bytes(pl) || !ws) return MOE_ERR_WORKSPACE_TOO_SMALL;
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_permute(pl, topk_idx, p->num_src_blocks > 1 ? src_block : nullptr, p->topk, counts, offsets,
-                                sorted_to_flat, flat_to_sorted, (int32_t*)ws, s);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  e = launch_dispatch_copy(x, M, (int64_t)p->hidden * elem_bytes(p), p->topk, flat_to_sorted, x_perm, s);
-  return hip_status(e);
+  if (ws_bytes < permute_ws_bytes(plan_of(p)) || !ws) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  return dispatch_launch(p, x, topk_idx, src_block, counts, offsets, sorted_to_flat, flat_to_sorted, x_perm, ws,
+                         (hipStream_t)stream);
 }
 
 moe_status_t moe_grouped_gemm(const moe_problem_t* p, int32_t layer, const void* a, const void* w0, const void* w1,
@@ -201,6 +281,10 @@ moe_status_t moe_grouped_gemm(const moe_problem_t* p, int32_t layer, const void*
   gp.ws = ws;
   gp.ws_bytes = ws ? ws_bytes : 0;
   hipStream_t s = (hipStream_t)stream;
+  if (debug_validate()) {
+    st = validate_offsets(p, offsets, s);
+    if (st != MOE_OK) return st;
+  }
   if (is_mx(p)) return hip_status(launch_grouped_gemm_mx(gp, s));
   return hip_status(p->dtype == MOE_DTYPE_BF16 ? launch_grouped_gemm_bf16(gp, s) : launch_grouped_gemm_f32(gp, s));
 }
@@ -215,6 +299,11 @@ moe_status_t moe_combine_ex(const moe_problem_t* p, const float* y, const float*
   OutEpilogue ep;
   st = epilogue_of(p, epi, out, &ep);
   if (st != MOE_OK) return st;
+  if (debug_validate()) {
+    st = check_range(flat_to_sorted, p->num_tokens * (int64_t)p->topk, -1, (int32_t)(p->num_tokens * p->topk),
+                     (hipStream_t)stream);
+    if (st != MOE_OK) return st;
+  }
   return hip_status(launch_combine(y, topk_w, flat_to_sorted, p->num_tokens, p->hidden, p->topk, ep,
                                    (hipStream_t)stream));
 }
@@ -275,6 +364,11 @@ moe_status_t moe_layer_ex(const moe_problem_t* p, const void* x, const float* lo
   o.spin_limit = 0;
   if (opts) o = *opts;
 
+  if (debug_validate() && M > 0) {
+    st = validate_logits(p, (const float*)logits, s);
+    if (st == MOE_OK && p->num_src_blocks > 1) st = check_range(src_block, M, 0, p->num_src_blocks, s);
+    if (st != MOE_OK) return st;
+  }
   // cleared with a fill kernel rather than a memset node, so that the call
   // can be captured into a HIP graph
   hipError_t e = launch_fill_i32(status, 1, 0, s);
@@ -287,10 +381,6 @@ moe_status_t moe_layer_ex(const moe_problem_t* p, const void* x, const float* lo
   }
   e = launch_route(logits, M, p->num_experts, p->topk, idx, w, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  const PermutePlan pl = plan_of(p);
-  e = launch_permute(pl, idx, src, p->topk, counts, offsets, s2f, f2s, at<int32_t>(ws, L.perm), s);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-
   const int cus = device_cu_count();
   // n_mover < 0 asks the profiled table, which may pick the kernel chain
   const int movers = o.n_mover >= 0 ? o.n_mover
@@ -326,13 +416,13 @@ moe_status_t moe_layer_ex(const moe_problem_t* p, const void* x, const float* lo
     if (fs != MOE_OK) return fs;
     // the fused kernel reads token rows straight from x; X_perm is produced
     // only when the caller asks for it
-    if (a.x_perm) {
-      e = launch_dispatch_copy(x, M, (int64_t)p->hidden * elem_bytes(p), p->topk, f2s, xp, s);
-      if (e != hipSuccess) return MOE_ERR_HIP;
-    }
+    e = launch_dispatch(plan_of(p), idx, src, counts, offsets, s2f, f2s, x, (int64_t)p->hidden * elem_bytes(p),
+                        a.x_perm ? xp : nullptr, at<int32_t>(ws, L.perm), s);
+    if (e != hipSuccess) return MOE_ERR_HIP;
     return hip_status(launch_fused_layer(fa, s));
   }
-  e = launch_dispatch_copy(x, M, (int64_t)p->hidden * elem_bytes(p), p->topk, f2s, xp, s);
+  e = launch_dispatch(plan_of(p), idx, src, counts, offsets, s2f, f2s, x, (int64_t)p->hidden * elem_bytes(p), xp,
+                      at<int32_t>(ws, L.perm), s);
   if (e != hipSuccess) return MOE_ERR_HIP;
   GemmProblem gp;
   gp.R = M * p->topk;

@@ -6,8 +6,8 @@
 // accumulation back into token order).
 //   out[t, n] = sum_{j<k} w[t,j] * Y[flat_to_sorted[t*k+j], n]
 // in f32, from zero, j increasing, one fused multiply-add per term, over
-// the slots whose pair is held here; then the epilogue (optional residual
-// add, f32 or bf16 output).
+// the slots whose pair is held here (a row index outside [0, M k) counts as
+// not held); then the epilogue (optional residual add, f32 or bf16 output).
 // A block walks whole token rows, 4 columns per lane per step, so every
 // Y row read and every out row write is contiguous.
 #include "common.hpp"
@@ -40,7 +40,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
       for (int u = 0; u < kCombineUnroll; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
       for (int j = 0; j < k; ++j) {
         const int32_t row = rows[j];
-        if (row < 0) continue;
+        if ((uint64_t)(int64_t)row >= (uint64_t)(M * k)) continue;  // -1: a pair of an expert not held here
         const float wj = w[j];
         const float* yr = y + (int64_t)row * H;
         float4 v[kCombineUnroll];

@@ -76,12 +76,14 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float 
 
 // Top-k weighted reduction of one 4-wide column group, shared by the
 // stand-alone combine and the fused layer so both give identical bits.
-// A slot whose row is -1 (a pair of an expert not held here) is left out.
+// A slot whose row is -1 (a pair of an expert not held here), or any row
+// outside [0, R), is left out.
 __device__ __forceinline__ float4 combine_group(const float* __restrict__ y, const float* __restrict__ w,
-                                                const int32_t* __restrict__ rows, int k, int64_t H, int64_t n) {
+                                                const int32_t* __restrict__ rows, int k, int64_t H, int64_t n,
+                                                int64_t R) {
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int j = 0; j < k; ++j) {
-    if (rows[j] < 0) continue;
+    if ((uint64_t)(int64_t)rows[j] >= (uint64_t)R) continue;
     const float wj = w[j];
     const float4 v = *reinterpret_cast<const float4*>(y + (int64_t)rows[j] * H + n);
     acc.x = fmaf(wj, v.x, acc.x);

@@ -57,7 +57,7 @@ __device__ __forceinline__ bool split_pays(int nk, int s, bool halfable) {
 template <int LAYER, bool OUT8 = false>
 __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(Bf16GemmArgs args,
                                                                          const int32_t* __restrict__ offsets, int G,
-                                                                         int group_cols, SplitWs split) {
+                                                                         int xcd_slots, SplitWs split) {
   __shared__ __attribute__((aligned(16))) char lds[kGemmLdsBytes];
   __shared__ TileLds tl;
   const int NT = (args.N + (LAYER == 0 ? kL0Cols : kL1Cols) - 1) / (LAYER == 0 ? kL0Cols : kL1Cols);
@@ -79,11 +79,11 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(Bf16Gem
       const int entries = tail0 + r * s;
       for (int v = xcd_slot(blockIdx.x, grid); v < entries; v += grid) {
         if (v < tail0) {
-          const TileCoord c = tile_coord(v, G, NT, kTileRows, group_cols, rtb, tl);
+          const TileCoord c = tile_coord(v, G, NT, kTileRows, xcd_slots, rtb, tl);
           bf16_gemm_row_tile<LAYER>(args, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], c.m0, c.nt, lds);
         } else {
           const int u = v - tail0, jj = u / s, ck = u - jj * s;
-          const TileCoord c = tile_coord(tail0 + jj, G, NT, kTileRows, group_cols, rtb, tl);
+          const TileCoord c = tile_coord(tail0 + jj, G, NT, kTileRows, xcd_slots, rtb, tl);
           if (ck == 0 && threadIdx.x == 0) {
             int32_t* d = split.desc + 4 * jj;
             d[0] = tl.seg_start[c.g];
@@ -103,11 +103,11 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(Bf16Gem
   const int entries = T + half;
   for (int v = xcd_slot(blockIdx.x, grid); v < entries; v += grid) {
     if (v < T - half) {
-      const TileCoord c = tile_coord(v, G, NT, kTileRows, group_cols, rtb, tl);
+      const TileCoord c = tile_coord(v, G, NT, kTileRows, xcd_slots, rtb, tl);
       bf16_gemm_row_tile<LAYER, false, OUT8>(args, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], c.m0, c.nt, lds);
     } else {
       const int j = v - (T - half);
-      const TileCoord c = tile_coord(T - half + j / 2, G, NT, kTileRows, group_cols, rtb, tl);
+      const TileCoord c = tile_coord(T - half + j / 2, G, NT, kTileRows, xcd_slots, rtb, tl);
       const int m0 = c.m0 + (j & 1) * (kTileRows / 2);
       if (m0 < tl.seg_rows[c.g])
         bf16_gemm_tile<LAYER, false, kTileRows / 2, false, OUT8>(args, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], m0,
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(Bf16Gem
 // tile; no split of the last round.
 __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_mx_kernel(Bf16GemmArgs args,
                                                                        const int32_t* __restrict__ offsets, int G,
-                                                                       int group_cols) {
+                                                                       int xcd_slots) {
   __shared__ __attribute__((aligned(16))) char lds[kGemmLdsBytes];
   __shared__ TileLds tl;
   const int NT = (args.N + kL1Cols - 1) / kL1Cols;
@@ -134,14 +134,14 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_mx_kernel(Bf16GemmA
   const int entries = T + half;
   for (int v = xcd_slot(blockIdx.x, grid); v < entries; v += grid) {
     if (v < T - half) {
-      const TileCoord c = tile_coord(v, G, NT, kTileRows, group_cols, rtb, tl);
+      const TileCoord c = tile_coord(v, G, NT, kTileRows, xcd_slots, rtb, tl);
       if (tl.seg_rows[c.g] <= kTileRows / 2)
         mx_gemm_tile<kTileRows / 2>(args, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], c.m0, c.nt, lds);
       else
         mx_gemm_tile<kTileRows>(args, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], c.m0, c.nt, lds);
     } else {
       const int j = v - (T - half);
-      const TileCoord c = tile_coord(T - half + j / 2, G, NT, kTileRows, group_cols, rtb, tl);
+      const TileCoord c = tile_coord(T - half + j / 2, G, NT, kTileRows, xcd_slots, rtb, tl);
       const int m0 = c.m0 + (j & 1) * (kTileRows / 2);
       if (m0 < tl.seg_rows[c.g]) mx_gemm_tile<kTileRows / 2>(args, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], m0, c.nt, lds);
     }
@@ -346,7 +346,7 @@ hipError_t launch_grouped_gemm_bf16(const GemmProblem& gp, hipStream_t s) {
   a.w_scale = nullptr;
   a.a_scale_bytes = a.w_scale_bytes = 0;
   const int grid = device_cu_count();
-  const int group_cols = grid / kXcds > 0 ? grid / kXcds : 1;
+  const int xcd_slots = grid / kXcds > 0 ? grid / kXcds : 1;
   SplitWs sp{nullptr, nullptr, nullptr};
   // layer 1 only; the header holds descriptors of up to 4096 split tiles (fewer than the grid)
   if (gp.layer == 1 && gp.ws && gp.ws_bytes >= gemm_split_ws_bytes() && grid <= 4096) {
@@ -356,9 +356,9 @@ hipError_t launch_grouped_gemm_bf16(const GemmProblem& gp, hipStream_t s) {
     sp.part = reinterpret_cast<float*>(w + kSplitHdrBytes);
   }
   if (gp.layer == 0)
-    grouped_gemm_bf16_kernel<0><<<grid, kGemmThreads, 0, s>>>(a, gp.offsets, gp.G, group_cols, sp);
+    grouped_gemm_bf16_kernel<0><<<grid, kGemmThreads, 0, s>>>(a, gp.offsets, gp.G, xcd_slots, sp);
   else
-    grouped_gemm_bf16_kernel<1><<<grid, kGemmThreads, 0, s>>>(a, gp.offsets, gp.G, group_cols, sp);
+    grouped_gemm_bf16_kernel<1><<<grid, kGemmThreads, 0, s>>>(a, gp.offsets, gp.G, xcd_slots, sp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !sp.hdr) return e;
   grouped_gemm_split_reduce<<<grid, 256, 0, s>>>(a, sp);
@@ -379,7 +379,7 @@ hipError_t launch_grouped_gemm_mx(const GemmProblem& gp, hipStream_t s) {
   a.w_scale = nullptr;
   a.a_scale_bytes = a.w_scale_bytes = 0;
   const int grid = device_cu_count();
-  const int group_cols = grid / kXcds > 0 ? grid / kXcds : 1;
+  const int xcd_slots = grid / kXcds > 0 ? grid / kXcds : 1;
   if (gp.layer == 0) {
     // x_perm, W_gate, W_up bf16; Hact MXFP8: R*F codes, then the scales
     a.a = (const __bf16*)gp.a;
@@ -387,7 +387,7 @@ hipError_t launch_grouped_gemm_mx(const GemmProblem& gp, hipStream_t s) {
     a.w1 = (const __bf16*)gp.w1;
     a.c = gp.c;
     a.c_scale = reinterpret_cast<uint8_t*>(gp.c) + gp.R * gp.N;
-    grouped_gemm_bf16_kernel<0, true><<<grid, kGemmThreads, 0, s>>>(a, gp.offsets, gp.G, group_cols, SplitWs{});
+    grouped_gemm_bf16_kernel<0, true><<<grid, kGemmThreads, 0, s>>>(a, gp.offsets, gp.G, xcd_slots, SplitWs{});
   } else {
     // Hact and W_down MXFP8 (codes, then scales); Y f32
     a.a = (const __bf16*)gp.a;
@@ -398,7 +398,7 @@ hipError_t launch_grouped_gemm_mx(const GemmProblem& gp, hipStream_t s) {
     a.w_scale_bytes = (uint32_t)mx_scale_bytes((int64_t)gp.E * gp.N, gp.K);
     a.w1 = nullptr;
     a.c = gp.c;
-    grouped_gemm_mx_kernel<<<grid, kGemmThreads, 0, s>>>(a, gp.offsets, gp.G, group_cols);
+    grouped_gemm_mx_kernel<<<grid, kGemmThreads, 0, s>>>(a, gp.offsets, gp.G, xcd_slots);
   }
   return hipGetLastError();
 }

@@ -13,26 +13,31 @@ namespace moe {
 hipError_t launch_route(const float* logits, int64_t M, int E, int k, int32_t* topk_idx, float* topk_w,
                         hipStream_t s);
 
-// Segment bookkeeping: per-chunk histograms, scan, stable ranks.  Pairs of
-// experts outside [base, base + EL) are dropped: they form an extra last
-// segment (index G) inside the bookkeeping, which is not reported.
+// Dispatch: segment bookkeeping (per-chunk histograms, bases, stable ranks)
+// and the copy of token rows to their sorted positions.  Pairs of experts
+// outside [base, base + EL) are dropped: they form an extra last segment
+// (index G) inside the bookkeeping, which is not reported.
 struct PermutePlan {
+  int64_t M;
+  int k;
   int64_t R;
-  int G;       // segments reported: S * EL
-  int Gi;      // segments ranked: G, or G + 1 when some experts are not held
-  int EL;      // experts held
-  int base;    // first expert held
-  int chunk;   // pairs per block
-  int blocks;  // ceil(R / chunk)
+  int G;        // segments reported: S * EL
+  int Gi;       // segments ranked: G, or G + 1 when some experts are not held
+  int EL;       // experts held
+  int base;     // first expert held
+  int Tc;       // tokens per chunk (a histogram each)
+  int Ts;       // tokens per dispatch workgroup
+  int blocks;   // chunks: ceil(M / Tc)
+  int64_t wgs;  // dispatch workgroups: ceil(M / Ts)
+  int scanned;  // a scan kernel turns the histograms into bases first
 };
 PermutePlan permute_plan(int64_t M, int k, int S, int E, int base, int EL);
 size_t permute_ws_bytes(const PermutePlan& pl);
-hipError_t launch_permute(const PermutePlan& pl, const int32_t* topk_idx, const int32_t* src_block, int k,
-                          int32_t* counts, int32_t* offsets, int32_t* sorted_to_flat, int32_t* flat_to_sorted,
-                          int32_t* ws, hipStream_t s);
-// Rows of dropped pairs (flat_to_sorted -1) are not written.
-hipError_t launch_dispatch_copy(const void* x, int64_t M, int64_t row_bytes, int k, const int32_t* flat_to_sorted,
-                                void* x_perm, hipStream_t s);
+// x_perm null: the bookkeeping only (x is not read).  Rows of dropped pairs
+// (flat_to_sorted -1) are not written.
+hipError_t launch_dispatch(const PermutePlan& pl, const int32_t* topk_idx, const int32_t* src_block,
+                           int32_t* counts, int32_t* offsets, int32_t* sorted_to_flat, int32_t* flat_to_sorted,
+                           const void* x, int64_t row_bytes, void* x_perm, int32_t* ws, hipStream_t s);
 
 // Grouped GEMM (layer 0: gate/up + SwiGLU; layer 1: down).
 struct GemmProblem {
@@ -55,8 +60,10 @@ size_t gemm_split_ws_bytes();
 hipError_t launch_grouped_gemm_bf16(const GemmProblem& gp, hipStream_t s);
 hipError_t launch_grouped_gemm_f32(const GemmProblem& gp, hipStream_t s);
 // MXFP8 activation path: layer 0 bf16 -> Hact MXFP8; layer 1 MXFP8 x MXFP8 -> Y.
-// An MXFP8 tensor of rows x cols is one buffer: codes, then cols/32 scale
-// bytes per row.
+// An MXFP8 tensor of rows x cols (cols a multiple of 128) is one buffer: the
+// rows*cols codes, then the scale bytes in groups of 32 rows (rows padded to
+// a multiple of 32): the byte of row r, block b sits at
+// (r / 32) * cols + (b / 4) * 128 + (r % 32) * 4 + b % 4.
 hipError_t launch_grouped_gemm_mx(const GemmProblem& gp, hipStream_t s);
 hipError_t launch_mx_quantize(const void* src, int src_bf16, int64_t rows, int cols, void* dst, hipStream_t s);
 

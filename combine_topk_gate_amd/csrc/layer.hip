@@ -160,7 +160,7 @@ __device__ void combine_chunk(const FusedArgs& a, int c, int64_t t0, int64_t t1,
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int i = min(i0 + u, nt - 1);
-        o[u] = combine_group(a.y, w_lds + i * k, rows_lds + i * k, k, a.H, n);
+        o[u] = combine_group(a.y, w_lds + i * k, rows_lds + i * k, k, a.H, n, a.M * k);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u)
@@ -208,14 +208,14 @@ __global__ __launch_bounds__(kGemmThreads) void fused_layer_kernel(FusedArgs a) 
   for (int c = 0; c < nc; ++c) total += MT * chunk_width(c) + ((dedicated || c == 0) ? 0 : CB);
   if (!dedicated) total += CB;
   const int W = gridDim.x - a.n_mover;
-  const int group_cols = W / kXcds > 0 ? W / kXcds : 1;
+  const int xcd_slots = W / kXcds > 0 ? W / kXcds : 1;
   // The queue is dealt to the XCDs in runs of `run` items (run r to queue
   // r % nq), and the workgroups of one XCD (hardware ids b with the same
   // b % 8) claim from their queue's counter: the tiles running at once on
   // an XCD are neighbours in the order and share its L2.  Claims stay in
   // increasing order per queue, which keeps the no-deadlock argument.
   const int nq = ((W % kXcds) == 0 && (a.n_mover % kXcds) == 0) ? kXcds : 1;
-  const int run = group_cols;
+  const int run = xcd_slots;
   const int q = (nq == 1) ? 0 : (int)(blockIdx.x % kXcds);
   int32_t* my_q = xcd_q + q;
   Bf16GemmArgs ga;
@@ -228,7 +228,7 @@ __global__ __launch_bounds__(kGemmThreads) void fused_layer_kernel(FusedArgs a) 
     const int v = (i / run) * (nq * run) + q * run + (i % run);
     if (v >= total) return;
     if (v < T0) {
-      const TileCoord c = tile_coord(v, a.G, nt0, kTileRows, group_cols, (int64_t)kTileRows * a.H * 2, tl);
+      const TileCoord c = tile_coord(v, a.G, nt0, kTileRows, xcd_slots, (int64_t)kTileRows * a.H * 2, tl);
       ga.a = reinterpret_cast<const __bf16*>(a.x);
       ga.w0 = reinterpret_cast<const __bf16*>(a.w_gate);
       ga.w1 = reinterpret_cast<const __bf16*>(a.w_up);
@@ -261,7 +261,7 @@ __global__ __launch_bounds__(kGemmThreads) void fused_layer_kernel(FusedArgs a) 
       }
     }
     if (is_tile) {
-      const TileCoord c = tile_coord(u, a.G, chunk_width(chunk), kTileRows, group_cols, (int64_t)kTileRows * a.F * 2, tl);
+      const TileCoord c = tile_coord(u, a.G, chunk_width(chunk), kTileRows, xcd_slots, (int64_t)kTileRows * a.F * 2, tl);
       if (!block_wait(l0done + c.mt, nt0, a.status, limit, &lds_word)) return;
       ga.a = reinterpret_cast<const __bf16*>(a.hact);
       ga.w0 = reinterpret_cast<const __bf16*>(a.w_down);

@@ -11,17 +11,25 @@
 // and the dropped pairs' flat_to_sorted entries are written as -1.
 //
 // No atomic operation decides an order, so every output is bit-exact and
-// independent of scheduling:
-//   seg_count  one block per chunk of pairs: LDS histogram over the G
-//              segments (atomics only add counts, which commute).
-//   seg_scan   one block: per segment, exclusive prefix over the chunks;
-//              counts; exclusive prefix over segments = offsets; the
-//              start of every (chunk, segment) run.
-//   seg_rank   one block per chunk, walking it 256 pairs at a time in flat
-//              order: inside a wave, lanes with equal keys find each other
-//              with one ballot per key bit, and the rank among them is a
-//              popcount of the lower lanes; waves are ordered through a small
-//              per-wave count table in LDS.
+// independent of scheduling.  The tokens are cut into chunks of Tc tokens
+// (Tc k pairs), and each chunk into workgroups of Ts tokens:
+//   seg_count       one block per chunk: LDS histogram over the segments
+//                   (atomics only add counts, which commute).
+//   dispatch_kernel one workgroup per Ts tokens.  It first issues the loads
+//                   of its first token rows, then derives its chunk's
+//                   segment bases from all chunks' histograms (segment
+//                   totals, their exclusive prefix = offsets, plus the
+//                   counts of earlier chunks), ranks the pairs from its
+//                   chunk's start to its last token in steps of 256 (lanes
+//                   with equal keys find each other with one ballot per key
+//                   bit, the rank among them is a popcount of the lower
+//                   lanes, waves are ordered through a per-wave count table
+//                   in LDS), writes the permutation entries of its own
+//                   pairs, and copies its token rows to their sorted
+//                   positions (each row read once, written k times).
+// When the histograms are too many for every workgroup to sum them
+// (chunks x segments past kMaxSummed), one more kernel, seg_scan, turns
+// them into the chunks' bases first and dispatch_kernel reads those.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -31,12 +39,15 @@ constexpr int kPermThreads = 256;
 constexpr int kPermWaves = kPermThreads / kWave;
 constexpr int kMaxSegments = 1024;
 
-// Segment of pair f; G (one past the reported segments) if dropped.
+// Segment of pair f; G (one past the reported segments) if dropped.  An
+// expert id or source block out of range (a caller's error, which
+// MOE_DEBUG_VALIDATE reports) also gives G, so the pair is ranked in the
+// dropped segment or not at all, and no index leaves its array.
 __device__ __forceinline__ int seg_of(const int32_t* __restrict__ topk_idx, const int32_t* __restrict__ src_block,
                                       int ebase, int EL, int G, int k, int64_t f) {
-  const int s = src_block ? src_block[f / k] : 0;
+  const unsigned s = src_block ? (unsigned)src_block[f / k] : 0u;
   const unsigned e = (unsigned)(topk_idx[f] - ebase);
-  return e < (unsigned)EL ? s * EL + (int)e : G;
+  return (e < (unsigned)EL && s < (unsigned)(G / EL)) ? (int)s * EL + (int)e : G;
 }
 
 // Histograms over the Gi ranked segments (Gi = G, or G + 1 with dropped pairs).
@@ -49,8 +60,10 @@ __global__ __launch_bounds__(kPermThreads) void seg_count_kernel(const int32_t* 
   __syncthreads();
   const int64_t begin = (int64_t)blockIdx.x * chunk;
   const int64_t end = (begin + chunk < R) ? begin + chunk : R;
-  for (int64_t f = begin + threadIdx.x; f < end; f += kPermThreads)
-    atomicAdd(&hist[seg_of(topk_idx, src_block, ebase, EL, G, k, f)], 1);
+  for (int64_t f = begin + threadIdx.x; f < end; f += kPermThreads) {
+    const int g = seg_of(topk_idx, src_block, ebase, EL, G, k, f);
+    if (g < Gi) atomicAdd(&hist[g], 1);
+  }
   __syncthreads();
   for (int g = threadIdx.x; g < Gi; g += kPermThreads) block_hist[(int64_t)blockIdx.x * Gi + g] = hist[g];
 }
@@ -108,7 +121,8 @@ __global__ __launch_bounds__(kMaxSegments) void seg_scan_kernel(int G, int Gr, i
     __syncthreads();
   }
   if (threadIdx.x < G && threadIdx.x <= Gr) offsets[threadIdx.x] = s[threadIdx.x] - total;
-  if (G == Gr && threadIdx.x == 0) offsets[Gr] = (int)R;
+  // every pair is ranked (R in total) unless an expert id was out of range
+  if (G == Gr && threadIdx.x == 0) offsets[Gr] = s[G - 1];
   __syncthreads();
   // block_hist[b][g] <- offsets[g] + pairs of segment g in blocks before b
   if (active && g < G) {
@@ -122,32 +136,139 @@ __global__ __launch_bounds__(kMaxSegments) void seg_scan_kernel(int G, int Gr, i
   }
 }
 
-// Ranks over the Gi ranked segments; a dropped pair (segment G) writes -1.
-__global__ __launch_bounds__(kPermThreads) void seg_rank_kernel(const int32_t* __restrict__ topk_idx,
-                                                                const int32_t* __restrict__ src_block, int ebase,
-                                                                int EL, int k, int64_t R, int G, int Gi, int chunk,
-                                                                int nbits,
-                                                                const int32_t* __restrict__ block_base,
-                                                                int32_t* __restrict__ sorted_to_flat,
-                                                                int32_t* __restrict__ flat_to_sorted) {
-  __shared__ int running[kMaxSegments];
-  __shared__ int wcnt[kPermWaves][kMaxSegments];
-  const int tid = threadIdx.x, w = tid / kWave;
-  for (int g = tid; g < Gi; g += kPermThreads) {
-    running[g] = block_base[(int64_t)blockIdx.x * Gi + g];
+// ------------------------------------------------------------ dispatch ---
+constexpr int kMaxOwnPairs = 256;      // pairs of one dispatch workgroup: Ts k <= 256
+constexpr int kMaxSummed = 16384;      // chunks x segments one workgroup sums itself
+constexpr int kMaxChunkPairs = 2048;   // pairs a workgroup ranks at most (8 steps of 256)
+constexpr int kCopyRows = 2;           // token rows per copy step (loads in flight per lane)
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+struct DispatchArgs {
+  const int32_t* topk_idx;
+  const int32_t* src_block;
+  int ebase, EL, k, G, Gi, nbits;
+  int64_t M;
+  int Tc, Ts, chunks;
+  const int32_t* hist;  // [chunks][Gi]: histograms, or (scanned) the chunks' bases
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* s2f;
+  int32_t* f2s;
+  const u32x4_t* x;  // token rows, C 16-byte units each; null: no copy
+  u32x4_t* xp;
+  int C;
+};
+
+// Exclusive prefix sum of v[0..n) in place (n <= kMaxSegments), done by
+// the first wave (lane l owns up to 16 consecutive entries; one shuffle scan
+// over the lanes), so the block waits at one barrier only; all threads call
+// it and get the total.  word: one int of LDS.
+__device__ int block_exclusive_scan(int* v, int n, int* word) {
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    const int per = (n + kWave - 1) / kWave;
+    const int i0 = lane * per, i1 = i0 + per < n ? i0 + per : n;
+    int run = 0;
+    for (int i = i0; i < i1; ++i) run += v[i];
+    int inc = run;
 #pragma unroll
-    for (int q = 0; q < kPermWaves; ++q) wcnt[q][g] = 0;
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int t = __shfl_up(inc, off);
+      if (lane >= off) inc += t;
+    }
+    int acc = inc - run;
+    for (int i = i0; i < i1; ++i) {
+      const int c = v[i];
+      v[i] = acc;
+      acc += c;
+    }
+    if (lane == kWave - 1) *word = inc;
   }
   __syncthreads();
-  const int64_t begin = (int64_t)blockIdx.x * chunk;
-  const int64_t end = (begin + chunk < R) ? begin + chunk : R;
+  return *word;
+}
+
+// UPR: 16-byte units of a token row per thread (rows of at most 256 UPR
+// units), so a batch of 16 / UPR rows sits in 16 registers of 16 bytes per
+// thread; 0: rows of any width, copied two rows at a time.
+template <bool SCANNED, int UPR>
+__global__ __launch_bounds__(kPermThreads) void dispatch_kernel(DispatchArgs a) {
+  __shared__ int base[kMaxSegments];              // next sorted position of each segment
+  __shared__ int tot[kMaxSegments];               // segment totals, then their prefix
+  __shared__ int wcnt[kPermWaves][kMaxSegments];  // pairs per wave and segment in the current step
+  __shared__ int pos_lds[kMaxOwnPairs];           // sorted position of each own pair (-1: none)
+  __shared__ int word;
+  const int tid = threadIdx.x, w = tid / kWave;
+  const int k = a.k, Gi = a.Gi;
+  const int64_t t0 = (int64_t)blockIdx.x * a.Ts;
+  const int64_t t1 = t0 + a.Ts < a.M ? t0 + a.Ts : a.M;
+  const int c = (int)(t0 / a.Tc);
+  const int64_t fbeg = (int64_t)c * a.Tc * k;  // first pair of the chunk
+  const int64_t own0 = t0 * k, own1 = t1 * k;  // own pairs
+
+  // (1) the first batch of token rows is loaded before the bookkeeping, so
+  // the loads are in flight meanwhile (a token none of whose experts is held
+  // here is not read)
+  constexpr int RB = UPR > 0 ? 16 / UPR : kCopyRows;  // rows per batch
+  constexpr int UU = UPR > 0 ? UPR : 2;               // units per thread per row and step
+  u32x4_t v[RB][UU];
+  const bool copy = a.x != nullptr;
+  if (copy) {
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      bool held = false;
+      if (t0 + r < t1)
+        for (int j = 0; j < k; ++j) held |= (unsigned)(a.topk_idx[(t0 + r) * k + j] - a.ebase) < (unsigned)a.EL;
+#pragma unroll
+      for (int u = 0; u < UU; ++u) {
+        const int cc = tid + u * kPermThreads;
+        if (held && cc < a.C) v[r][u] = a.x[(t0 + r) * a.C + cc];
+      }
+    }
+  }
+
+  // (2) bases of this chunk's segments
+  for (int g = tid; g < Gi; g += kPermThreads) {
+#pragma unroll
+    for (int q = 0; q < kPermWaves; ++q) wcnt[q][g] = 0;
+    if (SCANNED) base[g] = a.hist[(int64_t)c * Gi + g];
+    else base[g] = tot[g] = 0;
+  }
+  __syncthreads();
+  if (!SCANNED) {
+    const int n = a.chunks * Gi;
+    for (int i = tid; i < n; i += kPermThreads) {
+      const int b = i / Gi, g = i - b * Gi;
+      const int cnt = a.hist[i];
+      if (cnt) {
+        atomicAdd(&tot[g], cnt);
+        if (b < c) atomicAdd(&base[g], cnt);
+      }
+    }
+    __syncthreads();
+    if (blockIdx.x == 0)
+      for (int g = tid; g < a.G; g += kPermThreads) a.counts[g] = tot[g];
+    __syncthreads();
+    const int ranked = block_exclusive_scan(tot, Gi, &word);  // tot = offsets
+    for (int g = tid; g < Gi; g += kPermThreads) base[g] += tot[g];
+    if (blockIdx.x == 0) {
+      for (int g = tid; g < a.G; g += kPermThreads) a.offsets[g] = tot[g];
+      // the kept pairs end where the dropped pairs' segment starts, or with the last ranked pair
+      if (tid == 0) a.offsets[a.G] = a.G < Gi ? tot[a.G] : ranked;
+    }
+    __syncthreads();
+  }
+
+  // (3) ranks from the chunk's first pair to the last own pair
   const uint64_t below = lanemask_lt();
-  for (int64_t base = begin; base < end; base += kPermThreads) {
-    const int64_t f = base + tid;
-    const bool valid = f < end;
-    const int g = valid ? seg_of(topk_idx, src_block, ebase, EL, G, k, f) : 0;
+  for (int64_t sb = fbeg; sb < own1; sb += kPermThreads) {
+    const int64_t f = sb + tid;
+    const bool inr = f < own1;
+    const int gf = inr ? seg_of(a.topk_idx, a.src_block, a.ebase, a.EL, a.G, k, f) : Gi;
+    const bool valid = gf < Gi;  // an invalid expert id of a plain layer gets no position
+    const int g = valid ? gf : 0;
     uint64_t peers = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
+    for (int b = 0; b < a.nbits; ++b) {
       const int bit = (g >> b) & 1;
       const uint64_t ones = __ballot(valid && bit);
       peers &= bit ? ones : ~ones;
@@ -156,99 +277,88 @@ __global__ __launch_bounds__(kPermThreads) void seg_rank_kernel(const int32_t* _
     const int group = __popcll(peers);
     if (valid && rank == 0) wcnt[w][g] = group;
     __syncthreads();
-    if (valid) {
-      int pos = running[g] + rank;
-      for (int q = 0; q < w; ++q) pos += wcnt[q][g];
-      const bool kept = g < G;
-      sorted_to_flat[pos] = kept ? (int32_t)f : -1;
-      flat_to_sorted[f] = kept ? pos : -1;
+    if (inr && f >= own0) {
+      int pos = -1;
+      if (valid) {
+        pos = base[g] + rank;
+        for (int q = 0; q < w; ++q) pos += wcnt[q][g];
+        a.s2f[pos] = g < a.G ? (int32_t)f : -1;
+        if (g >= a.G) pos = -1;  // a pair of an expert not held here
+      }
+      a.f2s[f] = pos;
+      pos_lds[f - own0] = pos;
     }
     __syncthreads();
     if (valid && rank == 0) {
-      atomicAdd(&running[g], group);
+      atomicAdd(&base[g], group);
       wcnt[w][g] = 0;
     }
     __syncthreads();
   }
-}
+  if (!copy) return;
 
-PermutePlan permute_plan(int64_t M, int k, int S, int E, int base, int EL) {
-  PermutePlan pl;
-  pl.R = M * k;
-  pl.EL = EL > 0 ? EL : E;
-  pl.base = EL > 0 ? base : 0;
-  pl.G = S * pl.EL;
-  pl.Gi = pl.G + (pl.EL < E ? 1 : 0);
-  // small chunks: many blocks rank in parallel (the ranking of one chunk is
-  // sequential in steps of 256 pairs)
-  int64_t chunk = 512;
-  const int64_t want = (pl.R + 1023) / 1024;  // at most 1024 chunks
-  if (want > chunk) chunk = ((want + kPermThreads - 1) / kPermThreads) * kPermThreads;
-  pl.chunk = (int)chunk;
-  pl.blocks = (int)((pl.R + chunk - 1) / chunk);
-  return pl;
-}
-
-size_t permute_ws_bytes(const PermutePlan& pl) { return (size_t)(pl.blocks > 0 ? pl.blocks : 1) * pl.Gi * 4; }
-
-hipError_t launch_permute(const PermutePlan& pl, const int32_t* topk_idx, const int32_t* src_block, int k,
-                          int32_t* counts, int32_t* offsets, int32_t* sorted_to_flat, int32_t* flat_to_sorted,
-                          int32_t* ws, hipStream_t s) {
-  int nbits = 1;
-  while ((1 << nbits) < pl.Gi) ++nbits;
-  if (pl.blocks > 0)
-    seg_count_kernel<<<pl.blocks, kPermThreads, 0, s>>>(topk_idx, src_block, pl.base, pl.EL, k, pl.R, pl.G, pl.Gi,
-                                                        pl.chunk, ws);
-  seg_scan_kernel<<<1, kMaxSegments, 0, s>>>(pl.Gi, pl.G, pl.blocks, pl.R, ws, counts, offsets);
-  if (pl.blocks > 0)
-    seg_rank_kernel<<<pl.blocks, kPermThreads, 0, s>>>(topk_idx, src_block, pl.base, pl.EL, k, pl.R, pl.G, pl.Gi,
-                                                       pl.chunk, nbits, ws, sorted_to_flat, flat_to_sorted);
-  return hipGetLastError();
-}
-
-// ------------------------------------------------------------ dispatch ---
-// Each token row is read once and written to its k sorted positions,
-// 16 bytes per lane; a block walks whole rows (two at a time, so each lane
-// has several loads in flight) and the writes of one row are contiguous.
-// X_perm is written with ordinary stores (measured on MI355X: 33.7 us for
-// Mixtral's 201 MB against 39.7 us with non-temporal stores).
-constexpr int kCopyThreads = 256;
-constexpr int kCopyRows = 2;
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-
-__global__ __launch_bounds__(kCopyThreads) void dispatch_copy_kernel(const u32x4_t* __restrict__ x, int64_t M,
-                                                                     int C, int k, const int32_t* __restrict__ f2s,
-                                                                     u32x4_t* __restrict__ xp) {
-  for (int64_t t0 = (int64_t)blockIdx.x * kCopyRows; t0 < M; t0 += (int64_t)gridDim.x * kCopyRows) {
-    const int nr = (M - t0) < kCopyRows ? (int)(M - t0) : kCopyRows;
-    // a token none of whose pairs is held here is not read at all
-    bool need[kCopyRows];
+  // (4) the copy: each row read once and written to its kept positions
+  auto needed = [&](int64_t t) {
+    bool nd = false;
+    for (int j = 0; j < k; ++j) nd |= pos_lds[(t - t0) * k + j] >= 0;
+    return nd;
+  };
+  if constexpr (UPR > 0) {
+    for (int64_t tb = t0; tb < t1; tb += RB) {
+      if (tb != t0) {
 #pragma unroll
-    for (int r = 0; r < kCopyRows; ++r) {
-      need[r] = false;
-      if (r < nr)
-        for (int j = 0; j < k; ++j) need[r] |= f2s[(t0 + r) * k + j] >= 0;
+        for (int r = 0; r < RB; ++r) {
+          const bool nd = tb + r < t1 && needed(tb + r);
+#pragma unroll
+          for (int u = 0; u < UU; ++u) {
+            const int cc = tid + u * kPermThreads;
+            if (nd && cc < a.C) v[r][u] = a.x[(tb + r) * a.C + cc];
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        if (tb + r >= t1) continue;
+        for (int j = 0; j < k; ++j) {
+          const int row = pos_lds[(tb + r - t0) * k + j];
+          if (row < 0) continue;
+          u32x4_t* d = a.xp + (int64_t)row * a.C;
+#pragma unroll
+          for (int u = 0; u < UU; ++u) {
+            const int cc = tid + u * kPermThreads;
+            if (cc < a.C) d[cc] = v[r][u];
+          }
+        }
+      }
     }
-    for (int c0 = threadIdx.x; c0 < C; c0 += kCopyThreads * 2) {
-      u32x4_t v[kCopyRows][2];
+  } else {
+    for (int64_t tr = t0; tr < t1; tr += kCopyRows) {
+      const int nr = (t1 - tr) < kCopyRows ? (int)(t1 - tr) : kCopyRows;
+      bool need[kCopyRows];
 #pragma unroll
-      for (int r = 0; r < kCopyRows; ++r)
+      for (int r = 0; r < kCopyRows; ++r) need[r] = r < nr && needed(tr + r);
+      for (int c0 = tid; c0 < a.C; c0 += kPermThreads * 2) {
+        if (tr != t0 || c0 != tid) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int c = c0 + u * kCopyThreads;
-          if (need[r] && c < C) v[r][u] = x[(t0 + r) * C + c];
+          for (int r = 0; r < kCopyRows; ++r)
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              const int cc = c0 + u * kPermThreads;
+              if (need[r] && cc < a.C) v[r][u] = a.x[(tr + r) * a.C + cc];
+            }
         }
 #pragma unroll
-      for (int r = 0; r < kCopyRows; ++r) {
-        if (r >= nr || !need[r]) continue;
-        for (int j = 0; j < k; ++j) {
-          const int32_t row = f2s[(t0 + r) * k + j];
-          if (row < 0) continue;  // pair of an expert not held here
-          u32x4_t* d = xp + (int64_t)row * C;
+        for (int r = 0; r < kCopyRows; ++r) {
+          if (!need[r]) continue;
+          for (int j = 0; j < k; ++j) {
+            const int row = pos_lds[(tr - t0 + r) * k + j];
+            if (row < 0) continue;
+            u32x4_t* d = a.xp + (int64_t)row * a.C;
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const int c = c0 + u * kCopyThreads;
-            if (c < C) d[c] = v[r][u];
+            for (int u = 0; u < 2; ++u) {
+              const int cc = c0 + u * kPermThreads;
+              if (cc < a.C) d[cc] = v[r][u];
+            }
           }
         }
       }
@@ -256,14 +366,99 @@ __global__ __launch_bounds__(kCopyThreads) void dispatch_copy_kernel(const u32x4
   }
 }
 
-hipError_t launch_dispatch_copy(const void* x, int64_t M, int64_t row_bytes, int k, const int32_t* flat_to_sorted,
-                                void* x_perm, hipStream_t s) {
-  if (M == 0) return hipSuccess;
-  const int C = (int)(row_bytes / 16);
-  const int64_t pairs = (M + kCopyRows - 1) / kCopyRows;
-  const int64_t grid = pairs < 16384 ? pairs : 16384;
-  dispatch_copy_kernel<<<(unsigned)grid, kCopyThreads, 0, s>>>((const u32x4_t*)x, M, C, k, flat_to_sorted,
-                                                               (u32x4_t*)x_perm);
+// Tokens per chunk Tc (a multiple of 16) and per workgroup Ts (a power of
+// two up to 16, so Ts k <= kMaxOwnPairs for k <= 16).  Chunks of
+// about 512 pairs; at most 1024 of them; when every workgroup can sum the
+// histograms itself (chunks x segments <= kMaxSummed with chunks of at most
+// kMaxChunkPairs pairs) the chunks grow to make that so.
+PermutePlan permute_plan(int64_t M, int k, int S, int E, int base, int EL) {
+  PermutePlan pl;
+  pl.M = M;
+  pl.k = k;
+  pl.R = M * k;
+  pl.EL = EL > 0 ? EL : E;
+  pl.base = EL > 0 ? base : 0;
+  pl.G = S * pl.EL;
+  pl.Gi = pl.G + (pl.EL < E ? 1 : 0);
+  // about 1024 workgroups (4 per CU on 256 CUs, all resident, so every
+  // CU has enough row loads in flight), 2 to 16 tokens each
+  pl.Ts = 2;
+  while (pl.Ts < 16 && (int64_t)pl.Ts * 1024 < M) pl.Ts *= 2;
+  // chunks are whole multiples of 16 tokens, so of any Ts
+  auto round_up = [&](int64_t t) { return ((t + 15) / 16) * 16; };
+  int64_t Tc = round_up((512 + k - 1) / k);
+  const int64_t at_most = round_up((M + 1023) / 1024);  // at most 1024 chunks
+  if (at_most > Tc) Tc = at_most;
+  const int64_t summed = round_up((M * pl.Gi + kMaxSummed - 1) / kMaxSummed);
+  pl.scanned = 1;
+  if (summed * k <= kMaxChunkPairs) {
+    if (summed > Tc) Tc = summed;
+    pl.scanned = Tc * k > kMaxChunkPairs;
+  }
+  pl.Tc = (int)Tc;
+  pl.blocks = (int)((M + Tc - 1) / Tc);
+  pl.wgs = (M + pl.Ts - 1) / pl.Ts;
+  return pl;
+}
+
+size_t permute_ws_bytes(const PermutePlan& pl) { return (size_t)(pl.blocks > 0 ? pl.blocks : 1) * pl.Gi * 4; }
+
+hipError_t launch_dispatch(const PermutePlan& pl, const int32_t* topk_idx, const int32_t* src_block,
+                           int32_t* counts, int32_t* offsets, int32_t* sorted_to_flat, int32_t* flat_to_sorted,
+                           const void* x, int64_t row_bytes, void* x_perm, int32_t* ws, hipStream_t s) {
+  int nbits = 1;
+  while ((1 << nbits) < pl.Gi) ++nbits;
+  const int chunk = pl.Tc * pl.k;
+  if (pl.M == 0 || pl.scanned) {
+    if (pl.blocks > 0)
+      seg_count_kernel<<<pl.blocks, kPermThreads, 0, s>>>(topk_idx, src_block, pl.base, pl.EL, pl.k, pl.R, pl.G,
+                                                          pl.Gi, chunk, ws);
+    // with no tokens this only writes zero counts and offsets
+    seg_scan_kernel<<<1, kMaxSegments, 0, s>>>(pl.Gi, pl.G, pl.blocks, pl.R, ws, counts, offsets);
+    if (pl.M == 0) return hipGetLastError();
+  } else {
+    seg_count_kernel<<<pl.blocks, kPermThreads, 0, s>>>(topk_idx, src_block, pl.base, pl.EL, pl.k, pl.R, pl.G,
+                                                        pl.Gi, chunk, ws);
+  }
+  DispatchArgs a;
+  a.topk_idx = topk_idx;
+  a.src_block = src_block;
+  a.ebase = pl.base;
+  a.EL = pl.EL;
+  a.k = pl.k;
+  a.G = pl.G;
+  a.Gi = pl.Gi;
+  a.nbits = nbits;
+  a.M = pl.M;
+  a.Tc = pl.Tc;
+  a.Ts = pl.Ts;
+  a.chunks = pl.blocks;
+  a.hist = ws;
+  a.counts = counts;
+  a.offsets = offsets;
+  a.s2f = sorted_to_flat;
+  a.f2s = flat_to_sorted;
+  a.x = x_perm ? reinterpret_cast<const u32x4_t*>(x) : nullptr;
+  a.xp = reinterpret_cast<u32x4_t*>(x_perm);
+  a.C = (int)(row_bytes / 16);
+  const dim3 grid((unsigned)pl.wgs), block(kPermThreads);
+  // the narrowest register batch that holds a row's share of each thread
+  const int upr = a.C <= kPermThreads ? 1 : a.C <= 2 * kPermThreads ? 2 : a.C <= 4 * kPermThreads ? 4 : 0;
+  if (pl.scanned) {
+    switch (upr) {
+      case 1: dispatch_kernel<true, 1><<<grid, block, 0, s>>>(a); break;
+      case 2: dispatch_kernel<true, 2><<<grid, block, 0, s>>>(a); break;
+      case 4: dispatch_kernel<true, 4><<<grid, block, 0, s>>>(a); break;
+      default: dispatch_kernel<true, 0><<<grid, block, 0, s>>>(a); break;
+    }
+  } else {
+    switch (upr) {
+      case 1: dispatch_kernel<false, 1><<<grid, block, 0, s>>>(a); break;
+      case 2: dispatch_kernel<false, 2><<<grid, block, 0, s>>>(a); break;
+      case 4: dispatch_kernel<false, 4><<<grid, block, 0, s>>>(a); break;
+      default: dispatch_kernel<false, 0><<<grid, block, 0, s>>>(a); break;
+    }
+  }
   return hipGetLastError();
 }
 

@@ -10,7 +10,7 @@
 // A segment of n rows has ceil(n / rows) row tiles ("M-tiles"); mt_start[g]
 // is the exclusive prefix of the M-tile counts.  With NT column tiles, the
 // tiles of segment g occupy [mt_start[g] * NT, mt_start[g+1] * NT) of the
-// queue, in blocks of row tiles and column groups (tile_coord).  A
+// queue, row tiles fastest, in blocks of row tiles (tile_coord).  A
 // persistent workgroup walks virtual slots
 // it*grid + v, and v is chosen so that the workgroups of one XCD (hardware
 // ids w, w+8, ... are dispatched round-robin over the 8 XCDs) own a
@@ -90,22 +90,27 @@ constexpr int64_t kResidentWeightBytes = 128ll << 20;
 
 // Tile v of a queue over NT column tiles (per segment mt_g * NT tiles).
 // panel_bytes is the bytes of one tile's operand panel over the whole
-// reduction (tokens of a row tile, weights of a column tile: both 256 rows).
-// Inside a segment: column groups of group_cols / mt tiles with the row
-// tiles fastest, so each weight panel is read once while the segment's
-// token rows are re-read from the cache.  A segment of more than
-// group_cols / 4 row tiles whose token rows are too big for the cache, or
-// whose weight panels are small enough to be read twice from it, is cut
-// into nb = ceil(mt / (group_cols / 4)) blocks of row tiles of nearly equal
-// height, each ordered as a segment of its own (8 x 4 tiles per column
-// group for 32 slots, against one column of every row tile).  Block b holds
-// rows [b mt / nb, (b + 1) mt / nb), i.e. queue entries [row0 NT, row1 NT).
-__device__ inline TileCoord tile_coord(int v, int G, int NT, int rows, int group_cols, int64_t panel_bytes,
+// reduction (tokens of a row tile, weights of a column tile: both 256 rows);
+// xcd_slots is the number of tiles one XCD runs at once (its workgroups).
+// Inside a segment (or a row block of it, below) the order is column-major
+// with the row tiles fastest: consecutive entries are the row tiles of one
+// weight column tile, then of the next column tile, so the tiles an XCD runs
+// at once (a contiguous run of the order, see xcd_slot) share a few weight
+// panels and a few token panels in its L2, and each weight panel is read
+// once while the segment's token rows are re-read from the cache.  A
+// segment of more than xcd_slots / 4 row tiles whose token rows are too big
+// for the cache, or whose weight panels are small enough to be read twice
+// from it, is cut into nb = ceil(mt / (xcd_slots / 4)) blocks of row tiles
+// of nearly equal height, each ordered as a segment of its own (so an XCD's
+// run spans about 8 row tiles x 4 column tiles instead of one column of
+// every row tile).  Block b holds rows [b mt / nb, (b + 1) mt / nb), i.e.
+// queue entries [row0 NT, row1 NT).
+__device__ inline TileCoord tile_coord(int v, int G, int NT, int rows, int xcd_slots, int64_t panel_bytes,
                                        const TileLds& t) {
   const int g = find_segment(v, G, NT, t.mt_start);
   const int l = v - t.mt_start[g] * NT;
   const int mt = t.mt_start[g + 1] - t.mt_start[g];
-  const int rbmax = group_cols / 4 > 0 ? group_cols / 4 : 1;
+  const int rbmax = xcd_slots / 4 > 0 ? xcd_slots / 4 : 1;
   const bool block = panel_bytes > 0 && mt > rbmax &&
                      ((int64_t)mt * panel_bytes > kResidentRowBytes || (int64_t)NT * panel_bytes <= kResidentWeightBytes);
   int r0 = 0, rb = mt, lb = l;
@@ -120,15 +125,11 @@ __device__ inline TileCoord tile_coord(int v, int G, int NT, int rows, int group
     rb = row_of(b + 1) - r0;
     lb = l - r0 * NT;
   }
-  int gn = group_cols / rb;
-  if (gn < 1) gn = 1;
-  const int span = rb * gn;
-  const int grp = lb / span, rem = lb - grp * span;
   TileCoord c;
   c.g = g;
-  const int mi = r0 + rem % rb;
+  const int mi = r0 + lb % rb;
   c.m0 = mi * rows;
-  c.nt = grp * gn + rem / rb;
+  c.nt = lb / rb;
   c.mt = t.mt_start[g] + mi;
   return c;
 }

@@ -41,7 +41,17 @@
  *     status and enqueues nothing.  Device-resident inputs are trusted:
  *     logits must be finite, src_block values must lie in [0, S), topk_idx
  *     in [0, E), and offsets must be the exclusive prefix sum of the counts
- *     of the same call sequence.  Violating these is undefined behaviour.
+ *     of the same call sequence.  Violating these gives unspecified results
+ *     (the kernels keep every memory access inside the caller's buffers: an
+ *     out-of-range expert id or source block makes its pair a dropped one).
+ *   - MOE_DEBUG_VALIDATE=1 in the environment makes every entry point check
+ *     those device-resident inputs before it launches anything: it copies
+ *     them to host memory (synchronising `stream`) and returns
+ *     MOE_ERR_INVALID_ARGUMENT if logits are not finite (moe_route,
+ *     moe_layer), topk_idx is outside [0, E) or src_block outside [0, S)
+ *     (moe_dispatch, moe_layer), offsets do not start at 0, decrease, or
+ *     end past R (moe_grouped_gemm), or flat_to_sorted is outside [-1, R)
+ *     (moe_combine).  For debugging only: it synchronises and copies.
  *   - Symbols: M tokens, H hidden, F expert width, E experts routing
  *     chooses from, EL experts held by the call (local_experts, = E unless
  *     set), k = topk, S source blocks, G = S*EL segments, R = M*k routed

@@ -181,12 +181,15 @@ def permutation(topk_idx, E, S=1, src_block=None, expert_base=0, local_experts=0
     return s2f, f2s
 
 
-def dispatch(x, k, sorted_to_flat):
-    """Step 4: X_perm rows, a byte copy of the token rows."""
+def dispatch(x, k, sorted_to_flat, out=None):
+    """Step 4: X_perm rows, a byte copy of the token rows (rows of sorted
+    positions that hold no pair are written as zeros).  out: an optional
+    [M*k, H] buffer of x's dtype to write into."""
     x = np.ascontiguousarray(x)
     M, H = x.shape
     s2f = _c(sorted_to_flat, np.int32)
-    xp = np.empty((M * k, H), x.dtype)
+    xp = np.empty((M * k, H), x.dtype) if out is None else out
+    assert xp.shape == (M * k, H) and xp.dtype == x.dtype and xp.flags.c_contiguous
     _check(_load().orc_dispatch(M, H, k, x.dtype.itemsize, _p(x), _p(s2f), _p(xp)), "dispatch")
     return xp
 
@@ -235,17 +238,24 @@ def mx_scales(buf, rows, cols):
     return out
 
 
-def ffn_rows(x, w_gate, w_up, w_down, k, S, sorted_to_flat, offsets, rows):
-    """Steps 5-6 for the listed sorted rows: (hact [n,F], y [n,H]) in float64."""
+def ffn_rows(x, w_gate, w_up, w_down, k, S, sorted_to_flat, offsets, rows, w_down_mx=None):
+    """Steps 5-6 for the listed sorted rows: (hact [n,F], y [n,H]) in float64.
+    w_down_mx (an mx_quantize buffer of W_down) selects the MXFP8 activation
+    path, as in moe_layer."""
     x = np.ascontiguousarray(x)
     dt = _dtype_code(x)
     E, F, H = w_gate.shape
     wg, wu, wd = (np.ascontiguousarray(a, dtype=x.dtype) for a in (w_gate, w_up, w_down))
+    act_fp8 = 0
+    if w_down_mx is not None:
+        act_fp8 = 1
+        wd = _c(w_down_mx, np.uint8)
+        assert wd.size == mx_bytes(E * H, F)
     rows = _c(rows, np.int64)
     n = rows.shape[0]
     hact = np.empty((n, F), np.float64)
     y = np.empty((n, H), np.float64)
-    _check(_load().orc_ffn_rows(H, F, E, S, k, dt, 0, _p(x), _p(wg), _p(wu), _p(wd),
+    _check(_load().orc_ffn_rows(H, F, E, S, k, dt, act_fp8, _p(x), _p(wg), _p(wu), _p(wd),
                                 _p(_c(sorted_to_flat, np.int32)), _p(_c(offsets, np.int32)), n, _p(rows),
                                 _p(hact), _p(y)), "ffn_rows")
     return hact, y

@@ -245,13 +245,15 @@ static double load_elem(const void* base, int dtype, int64_t i) {
  * the same as taking the first k of the sort by the key (-logit, e).
  * Weights: softmax over the selected logits, shifted by the slot-0 logit.
  */
+#define ORC_MAX_EXPERTS 1024 /* size of the per-token selection arrays below */
+
 int orc_route(int64_t M, int E, int k, const float* logits, int32_t* topk_idx, float* topk_w) {
-  if (M < 0 || E < 1 || k < 1 || k > E) return ORC_EINVAL;
+  if (M < 0 || E < 1 || E > ORC_MAX_EXPERTS || k < 1 || k > E) return ORC_EINVAL;
 #pragma omp parallel for schedule(static)
   for (int64_t t = 0; t < M; ++t) {
     const float* row = logits + t * (int64_t)E;
-    char taken[1024];
-    int sel[1024];
+    char taken[ORC_MAX_EXPERTS];
+    int sel[ORC_MAX_EXPERTS];
     memset(taken, 0, (size_t)E);
     for (int j = 0; j < k; ++j) {
       int best = -1;

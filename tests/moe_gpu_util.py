@@ -33,15 +33,19 @@ def upload(d, device="cuda:0"):
     return {k: dev(v, device) for k, v in d.items()}
 
 
-def run_chain(cfg, g, device="cuda:0", gemm_ws=True):
+def run_chain(cfg, g, device="cuda:0", gemm_ws=True, nan_fill=True):
     """moe_route -> moe_dispatch -> moe_grouped_gemm(0) -> (1) -> moe_combine.
     g: dict of device tensors x, logits, src_block, w_gate, w_up, w_down.
     gemm_ws: give the grouped GEMM its workspace (the grid's last round is
     then split along k, as in moe_layer's chain); without it the GEMM runs
-    unsplit, which is what the fused kernel reproduces bit for bit."""
+    unsplit, which is what the fused kernel reproduces bit for bit.
+    nan_fill: X_perm, Hact and Y start as NaN, so a row below offsets[G]
+    that no tile writes stays NaN (rows past it, of pairs of experts not
+    held, are never written nor read)."""
     p = problem_of(cfg)
     M, k, H, F, G, R = cfg.M, cfg.k, cfg.H, cfg.F, cfg.S * cfg.EL, cfg.M * cfg.k
     act = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    fill = float("nan") if nan_fill else 0.0
     o = dict(
         topk_idx=torch.empty((M, k), dtype=torch.int32, device=device),
         topk_w=torch.empty((M, k), dtype=torch.float32, device=device),
@@ -49,11 +53,10 @@ def run_chain(cfg, g, device="cuda:0", gemm_ws=True):
         offsets=torch.empty(G + 1, dtype=torch.int32, device=device),
         sorted_to_flat=torch.empty(R, dtype=torch.int32, device=device),
         flat_to_sorted=torch.empty(R, dtype=torch.int32, device=device),
-        # zeroed: rows past the kept pairs (experts not held) are never written
-        x_perm=torch.zeros((R, H), dtype=act, device=device),
-        hact=torch.zeros((R, F), dtype=act, device=device),
-        y=torch.zeros((R, H), dtype=torch.float32, device=device),
-        out=torch.empty((M, H), dtype=torch.float32, device=device),
+        x_perm=torch.full((R, H), fill, dtype=act, device=device),
+        hact=torch.full((R, F), fill, dtype=act, device=device),
+        y=torch.full((R, H), fill, dtype=torch.float32, device=device),
+        out=torch.full((M, H), fill, dtype=torch.float32, device=device),
     )
     ws = torch.empty(max(moe.moe_workspace_bytes(p, moe.MOE_OP_DISPATCH), 4), dtype=torch.uint8, device=device)
     moe.moe_route(p, g["logits"], o["topk_idx"], o["topk_w"])
@@ -90,9 +93,10 @@ def run_layer(cfg, g, device="cuda:0", aux=False, **opts):
             offsets=torch.empty(G + 1, dtype=torch.int32, device=device),
             sorted_to_flat=torch.empty(R, dtype=torch.int32, device=device),
             flat_to_sorted=torch.empty(R, dtype=torch.int32, device=device),
-            x_perm=torch.zeros((R, H), dtype=act, device=device),
-            hact=torch.zeros((R, F), dtype=act, device=device),
-            y=torch.zeros((R, H), dtype=torch.float32, device=device),
+            # NaN: rows the layer does not write stay NaN
+            x_perm=torch.full((R, H), float("nan"), dtype=act, device=device),
+            hact=torch.full((R, F), float("nan"), dtype=act, device=device),
+            y=torch.full((R, H), float("nan"), dtype=torch.float32, device=device),
         )
     moe.moe_layer(p, g["x"], g["logits"], g.get("src_block"), g["w_gate"], g["w_up"], g["w_down"], out, ws, aux=a,
                   **opts)
@@ -112,3 +116,17 @@ def tolerances(cfg):
     """(relative Frobenius, max abs) bounds for outputs: bf16 layers with f32
     accumulation 5e-3 / 2e-2; the f32 layer 1e-5 relative."""
     return (5e-3, 2e-2) if cfg.dtype == "bf16" else (1e-5, None)
+
+
+def kept_rows(o):
+    """Number of sorted rows the chain wrote (offsets[G])."""
+    return int(o["offsets"][-1])
+
+
+def assert_written(o, M):
+    """Every row below offsets[G] of X_perm, Hact and Y, and every row of
+    out, was written (the NaN fill is gone) and is finite."""
+    n = kept_rows(o)
+    for key in ("x_perm", "hact", "y"):
+        assert bool(torch.isfinite(o[key][:n]).all()), key
+    assert bool(torch.isfinite(o["out"][:M]).all()), "out"

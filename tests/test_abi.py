@@ -175,3 +175,4 @@ def test_mx_buffer_size_matches_the_layout():
     assert moe.mx_bytes(32, 256) == 32 * 256 + 32 * 8
     assert moe.mx_bytes(33, 256) == 33 * 256 + 64 * 8
     assert moe.mx_bytes(0, 128) == 0
+

@@ -64,6 +64,7 @@ MUTANTS = {
     "ffn_reads_flat_row": ("int64_t t = sorted_to_flat[r] / k;\n    double* xrow", "int64_t t = r / k;\n    double* xrow"),
     "dispatch_wrong_token": ("int64_t t = sorted_to_flat[r] / k;\n    memcpy", "int64_t t = sorted_to_flat[r] % k;\n    memcpy"),
     "inverse_not_inverted": ("flat_to_sorted[sorted_to_flat[q]] = (int32_t)q;", "flat_to_sorted[q] = sorted_to_flat[q];"),
+    "dispatch_dropped_rows_not_zeroed": ("      memset((char*)x_perm + (size_t)r * row, 0, row);\n", ""),
     "offsets_inclusive": ("offsets[g + 1] = offsets[g] + counts[g];", "offsets[g + 1] = offsets[g] + counts[g] + (g == 0);"),
 }
 
@@ -80,6 +81,7 @@ def _checks():
         ("segments_S1", lambda: pins.test_segments_and_permutation_brute_force(37, 8, 2, 1)),
         ("segments_S8", lambda: pins.test_segments_and_permutation_brute_force(96, 16, 8, 8)),
         ("dispatch", pins.test_dispatch_is_bitwise_row_copy),
+        ("dispatch_held", lambda: pins.test_dispatch_with_held_experts_zero_fills_past_kept_pairs("bf16", 4, 4, 1)),
         ("dense_f32", lambda: pins.test_layer_matches_dense_brute_force("f32", 4, 2)),
         ("dense_bf16", lambda: pins.test_layer_matches_dense_brute_force("bf16", 6, 3)),
         ("dense_src_blocks", pins.test_layer_with_source_blocks_matches_dense),

@@ -175,6 +175,33 @@ def test_dispatch_is_bitwise_row_copy():
     assert np.array_equal(xp, d["x"][s2f // cfg.k])
 
 
+@pytest.mark.parametrize("dtype,base,EL,S", [("bf16", 4, 4, 1), ("f32", 0, 1, 2), ("bf16", 6, 2, 4)])
+def test_dispatch_with_held_experts_zero_fills_past_kept_pairs(dtype, base, EL, S):
+    """With held experts the sorted positions past the kept pairs hold no
+    pair (-1): their X_perm rows are zero, every kept row is its token's row
+    bit for bit (numpy fancy indexing, not the oracle's loop)."""
+    cfg, d = small_inputs(48, 64, 64, 8, 2, dtype, 17 + base, S=S)
+    idx, _ = oracle.route(d["logits"], cfg.k)
+    s2f, _ = oracle.permutation(idx, cfg.E, S, d["src_block"], base, EL)
+    kept = int(np.isin(idx, np.arange(base, base + EL)).sum())
+    assert 0 < kept < cfg.M * cfg.k
+    assert np.all(s2f[:kept] >= 0) and np.all(s2f[kept:] == -1)
+    # a stale buffer (all bits set) must come back with zero rows past the kept pairs
+    stale = np.empty((cfg.M * cfg.k, cfg.H), dtype=d["x"].dtype)
+    stale.view(np.uint8)[:] = 0xFF
+    xp = oracle.dispatch(d["x"], cfg.k, s2f, out=stale)
+    assert xp is stale
+    assert np.array_equal(xp[:kept], d["x"][s2f[:kept] // cfg.k])
+    assert not np.any(xp[kept:])
+
+
+def test_route_rejects_more_experts_than_its_selection_arrays():
+    with pytest.raises(ValueError):
+        oracle.route(np.zeros((2, 1025), np.float32), 2)
+    idx, w = oracle.route(np.zeros((2, 1024), np.float32), 3)
+    assert idx.tolist() == [[0, 1, 2], [0, 1, 2]]
+
+
 # ------------------------------------------------------------------ layer --
 
 @pytest.mark.parametrize("dtype,E,k", [("f32", 4, 2), ("f32", 8, 8), ("bf16", 4, 2), ("bf16", 6, 3), ("f32", 1, 1)])

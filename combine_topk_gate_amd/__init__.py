@@ -8,7 +8,7 @@ the stream given) straight through.  There is no fallback: if the library is
 missing, loading it raises.
 
 The entry points keep the C names: ``moe_route``, ``moe_dispatch``,
-``moe_grouped_gemm``, ``moe_combine``, ``moe_combine_ex``, ``moe_layer``,
+``moe_dispatch_noalloc``, ``moe_grouped_gemm``, ``moe_combine``, ``moe_combine_ex``, ``moe_layer``,
 ``moe_layer_ex`` (plus
 ``moe_workspace_bytes``, ``moe_layer_default_movers``,
 ``moe_debug_device_status``, ``moe_status_string``, ``moe_abi_version``).
@@ -36,7 +36,9 @@ MOE_OP_DISPATCH = 0
 MOE_OP_GROUPED_GEMM = 1
 MOE_OP_LAYER = 2
 
-EXPORTED = ("moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_grouped_gemm", "moe_combine", "moe_combine_ex",
+MOE_NOALLOC_SCRATCH_BYTES = 1 << 20
+
+EXPORTED = ("moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_dispatch_noalloc", "moe_grouped_gemm", "moe_combine", "moe_combine_ex",
             "moe_layer", "moe_layer_ex", "moe_quantize_mxfp8", "moe_layer_default_movers", "moe_debug_device_status",
             "moe_status_string", "moe_abi_version")
 
@@ -85,6 +87,7 @@ def load_library(path: str = LIB_PATH):
         "moe_workspace_bytes": ([PP, I32], SZ),
         "moe_route": ([PP, P, P, P, P], I32),
         "moe_dispatch": ([PP, P, P, P, P, P, P, P, P, P, SZ, P], I32),
+        "moe_dispatch_noalloc": ([PP, P, P, P, P, P, P, P, P, P], I32),
         "moe_grouped_gemm": ([PP, I32, P, P, P, P, P, P, SZ, P], I32),
         "moe_combine": ([PP, P, P, P, P, P], I32),
         "moe_combine_ex": ([PP, P, P, P, ctypes.POINTER(Epilogue), P, P], I32),
@@ -181,6 +184,14 @@ def moe_dispatch(p, x, topk_idx, src_block, counts, offsets, sorted_to_flat, fla
     _check(load_library().moe_dispatch(ctypes.byref(p), _ptr(x), _ptr(topk_idx), _ptr(src_block), _ptr(counts),
                                        _ptr(offsets), _ptr(sorted_to_flat), _ptr(flat_to_sorted), _ptr(x_perm),
                                        _ptr(ws), _nbytes(ws), _stream(stream)), "moe_dispatch")
+
+
+def moe_dispatch_noalloc(p, x, topk_idx, src_block, counts, offsets, sorted_to_flat, flat_to_sorted, x_perm,
+                         stream=None):
+    _check(load_library().moe_dispatch_noalloc(ctypes.byref(p), _ptr(x), _ptr(topk_idx), _ptr(src_block),
+                                               _ptr(counts), _ptr(offsets), _ptr(sorted_to_flat),
+                                               _ptr(flat_to_sorted), _ptr(x_perm), _stream(stream)),
+           "moe_dispatch_noalloc")
 
 
 def moe_grouped_gemm(p, layer, a, w0, w1, offsets, c, ws=None, stream=None):

@@ -253,6 +253,18 @@ moe_status_t moe_dispatch(const moe_problem_t* p, const void* x, const int32_t* 
                          (hipStream_t)stream);
 }
 
+moe_status_t moe_dispatch_noalloc(const moe_problem_t* p, const void* x, const int32_t* topk_idx,
+                                  const int32_t* src_block, int32_t* counts, int32_t* offsets,
+                                  int32_t* sorted_to_flat, int32_t* flat_to_sorted, void* x_perm, void* stream) {
+  moe_status_t st = check_dispatch(p, x, topk_idx, src_block, counts, offsets, sorted_to_flat, flat_to_sorted, x_perm);
+  if (st != MOE_OK) return st;
+  if (permute_ws_bytes(plan_of(p)) > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_UNSUPPORTED;
+  void* scratch_addr = nullptr;
+  if (static_scratch(&scratch_addr) != hipSuccess) return MOE_ERR_HIP;
+  return dispatch_launch(p, x, topk_idx, src_block, counts, offsets, sorted_to_flat, flat_to_sorted, x_perm,
+                         scratch_addr, (hipStream_t)stream);
+}
+
 moe_status_t moe_grouped_gemm(const moe_problem_t* p, int32_t layer, const void* a, const void* w0, const void* w1,
                               const int32_t* offsets, void* c, void* ws, size_t ws_bytes, void* stream) {
   moe_status_t st = check_problem(p);

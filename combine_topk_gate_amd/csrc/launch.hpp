@@ -33,6 +33,9 @@ struct PermutePlan {
 };
 PermutePlan permute_plan(int64_t M, int k, int S, int E, int base, int EL);
 size_t permute_ws_bytes(const PermutePlan& pl);
+// Device address of this GPU's static scratch (MOE_NOALLOC_SCRATCH_BYTES),
+// looked up on the first call on each device.
+hipError_t static_scratch(void** addr);
 // x_perm null: the bookkeeping only (x is not read).  Rows of dropped pairs
 // (flat_to_sorted -1) are not written.
 hipError_t launch_dispatch(const PermutePlan& pl, const int32_t* topk_idx, const int32_t* src_block,

@@ -30,6 +30,8 @@
 // When the histograms are too many for every workgroup to sum them
 // (chunks x segments past kMaxSummed), one more kernel, seg_scan, turns
 // them into the chunks' bases first and dispatch_kernel reads those.
+#include <mutex>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -402,6 +404,38 @@ PermutePlan permute_plan(int64_t M, int k, int S, int E, int base, int EL) {
 }
 
 size_t permute_ws_bytes(const PermutePlan& pl) { return (size_t)(pl.blocks > 0 ? pl.blocks : 1) * pl.Gi * 4; }
+
+// ------------------------------------------------ static device scratch ---
+// Scratch of the allocation-free dispatch (moe_dispatch_noalloc): one
+// file-scope device array; every GPU the library runs on holds its own copy,
+// at its own address, until the process ends.  In host code `scratch` names
+// a host-side stand-in, not device memory, so it is never passed to a kernel
+// or a copy: the device address comes from hipGetSymbolAddress, looked up
+// once per device with that device current.
+static __device__ __align__(256) char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_addr[kMaxScratchDevices] = {};
+}  // namespace
+
+hipError_t static_scratch(void** addr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_dispatch(const PermutePlan& pl, const int32_t* topk_idx, const int32_t* src_block,
                            int32_t* counts, int32_t* offsets, int32_t* sorted_to_flat, int32_t* flat_to_sorted,

@@ -173,6 +173,27 @@ moe_status_t moe_dispatch(const moe_problem_t* p, const void* x, const int32_t* 
                           void* x_perm, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Allocation-free dispatch, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): moe_dispatch without the workspace argument.  Its scratch
+ * (the per-chunk segment histograms and their prefix sums) is a static
+ * device array of MOE_NOALLOC_SCRATCH_BYTES that the library holds on each
+ * GPU it runs on until the process ends; the call allocates nothing, and
+ * the kernels overwrite every scratch word they read, so nothing needs
+ * clearing between calls.  Problems whose dispatch workspace
+ * (moe_workspace_bytes(p, MOE_OP_DISPATCH)) exceeds that size return
+ * MOE_ERR_UNSUPPORTED before anything is enqueued.  All calls on one GPU
+ * share its scratch: calls that may run at the same time on one GPU (on
+ * different streams, or from different threads without ordering) race and
+ * must not be issued; calls ordered on one stream are fine.  Arguments,
+ * results and errors are otherwise those of moe_dispatch, bit for bit.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (1u << 20)
+moe_status_t moe_dispatch_noalloc(const moe_problem_t* p, const void* x, const int32_t* topk_idx,
+                                  const int32_t* src_block, int32_t* counts, int32_t* offsets,
+                                  int32_t* sorted_to_flat, int32_t* flat_to_sorted, void* x_perm, void* stream);
+
+/*
  * Grouped GEMM over the G segments ([GGEMM] C_i = A_i B_i with per-problem
  * sizes; segment g uses weight slot g % EL and rows offsets[g] ..
  * offsets[g+1]-1; rows from offsets[G] on are neither read nor written).

@@ -176,3 +176,25 @@ def test_mx_buffer_size_matches_the_layout():
     assert moe.mx_bytes(33, 256) == 33 * 256 + 64 * 8
     assert moe.mx_bytes(0, 128) == 0
 
+
+def test_noalloc_dispatch_checks_arguments_and_size_on_the_host(lib):
+    """moe_dispatch_noalloc rejects bad arguments and problems whose
+    bookkeeping exceeds its static scratch before touching the device."""
+    text = open(HEADER).read()
+    m = re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \(1u << (\d+)\)", text)
+    assert m and moe.MOE_NOALLOC_SCRATCH_BYTES == 1 << int(m.group(1))
+    fake, odd = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1002)
+    p = moe.problem(16, 64, 64, 8, 2)
+    f = lib.moe_dispatch_noalloc
+    assert f(ctypes.byref(p), fake, fake, None, None, fake, fake, fake, fake, None) == moe.MOE_ERR_INVALID_ARGUMENT
+    assert f(ctypes.byref(p), odd, fake, None, fake, fake, fake, fake, fake, None) == moe.MOE_ERR_INVALID_ARGUMENT
+    p2 = moe.problem(16, 64, 64, 8, 2, S=2)
+    assert f(ctypes.byref(p2), fake, fake, None, fake, fake, fake, fake, fake, None) == moe.MOE_ERR_INVALID_ARGUMENT
+    big = moe.problem(1 << 16, 64, 64, 64, 4, S=16)  # 512 chunks x 1024 segments
+    assert lib.moe_workspace_bytes(ctypes.byref(big), moe.MOE_OP_DISPATCH) > moe.MOE_NOALLOC_SCRATCH_BYTES
+    assert f(ctypes.byref(big), fake, fake, fake, fake, fake, fake, fake, fake, None) == moe.MOE_ERR_UNSUPPORTED
+    # the workloads of the benchmark fit
+    for (M, H, F, E, k, S) in [(8192, 4096, 14336, 8, 2, 1), (16384, 7168, 4096, 16, 8, 8), (4096, 2048, 1408, 64, 4, 1),
+                               (16384, 4096, 6400, 16, 2, 1)]:
+        q = moe.problem(M, H, F, E, k, S)
+        assert lib.moe_workspace_bytes(ctypes.byref(q), moe.MOE_OP_DISPATCH) <= moe.MOE_NOALLOC_SCRATCH_BYTES

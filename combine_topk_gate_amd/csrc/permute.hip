@@ -143,6 +143,10 @@ constexpr int kMaxOwnPairs = 256;      // pairs of one dispatch workgroup: Ts k 
 constexpr int kMaxSummed = 16384;      // chunks x segments one workgroup sums itself
 constexpr int kMaxChunkPairs = 2048;   // pairs a workgroup ranks at most (8 steps of 256)
 constexpr int kCopyRows = 2;           // token rows per copy step (loads in flight per lane)
+#ifndef MOE_DISPATCH_WGS
+#define MOE_DISPATCH_WGS 1024
+#endif
+constexpr int64_t kDispatchWgs = MOE_DISPATCH_WGS;  // workgroups the plan aims for
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 struct DispatchArgs {
@@ -238,13 +242,53 @@ __global__ __launch_bounds__(kPermThreads) void dispatch_kernel(DispatchArgs a) 
   }
   __syncthreads();
   if (!SCANNED) {
-    const int n = a.chunks * Gi;
-    for (int i = tid; i < n; i += kPermThreads) {
-      const int b = i / Gi, g = i - b * Gi;
-      const int cnt = a.hist[i];
-      if (cnt) {
-        atomicAdd(&tot[g], cnt);
-        if (b < c) atomicAdd(&base[g], cnt);
+    // per segment, the sum of its counts over all chunks (tot) and over the
+    // chunks before this one (base): with at most 256 segments, P threads
+    // per segment each sum a slice of the chunks (independent loads, all in
+    // flight), then the P partial sums are added; with more, one thread per
+    // segment walks every chunk
+    int gp = 1;
+    while (gp < Gi) gp <<= 1;
+    if (gp <= kPermThreads) {
+      const int P = kPermThreads / gp, g = tid % gp, q = tid / gp;
+      const int L = (a.chunks + P - 1) / P;
+      const int b0 = q * L, b1 = b0 + L < a.chunks ? b0 + L : a.chunks;
+      int sb = 0, sa = 0;
+      if (g < Gi) {
+#pragma unroll 8
+        for (int b = b0; b < b1; ++b) {
+          const int v = a.hist[(int64_t)b * Gi + g];
+          if (b < c) sb += v;
+          else sa += v;
+        }
+      }
+      wcnt[0][tid] = sb;
+      wcnt[1][tid] = sa;
+      __syncthreads();
+      if (q == 0 && g < Gi) {
+        int before = 0, after = 0;
+        for (int r = 0; r < P; ++r) {
+          before += wcnt[0][r * gp + g];
+          after += wcnt[1][r * gp + g];
+        }
+        base[g] = before;
+        tot[g] = before + after;
+      }
+      __syncthreads();
+      // the two rows of partial sums back to the zeros the ranking starts from
+      wcnt[0][tid] = 0;
+      wcnt[1][tid] = 0;
+    } else {
+      for (int g = tid; g < Gi; g += kPermThreads) {
+        int sb = 0, sa = 0;
+#pragma unroll 8
+        for (int b = 0; b < a.chunks; ++b) {
+          const int v = a.hist[(int64_t)b * Gi + g];
+          if (b < c) sb += v;
+          else sa += v;
+        }
+        base[g] = sb;
+        tot[g] = sb + sa;
       }
     }
     __syncthreads();
@@ -385,7 +429,7 @@ PermutePlan permute_plan(int64_t M, int k, int S, int E, int base, int EL) {
   // about 1024 workgroups (4 per CU on 256 CUs, all resident, so every
   // CU has enough row loads in flight), 2 to 16 tokens each
   pl.Ts = 2;
-  while (pl.Ts < 16 && (int64_t)pl.Ts * 1024 < M) pl.Ts *= 2;
+  while (pl.Ts < 16 && (int64_t)pl.Ts * kDispatchWgs < M) pl.Ts *= 2;
   // chunks are whole multiples of 16 tokens, so of any Ts
   auto round_up = [&](int64_t t) { return ((t + 15) / 16) * 16; };
   int64_t Tc = round_up((512 + k - 1) / k);

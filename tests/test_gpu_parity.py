@@ -188,10 +188,10 @@ EDGE = {
     "src_blocks_empty_segment": dict(M=256, H=128, F=128, E=4, k=2, S=8, bias=[0, 0, 0, -60]),
     "f32_ragged": dict(M=77, H=64, F=192, E=5, k=3, dtype="f32"),
     "k16_E64": dict(M=40, H=64, F=64, E=64, k=16),
-    # one partial round of layer-1 tiles, split 8 ways along F (36 steps: uneven ranges)
-    "split_single_round": dict(M=300, H=512, F=2304, E=4, k=2),
-    # ... with empty experts and ragged segments (50 steps)
-    "split_empty_experts": dict(M=200, H=256, F=3200, E=8, k=2, bias=[4, 4, 0, 0, -50, -50, 0, -50]),
+    # one partial round of layer-1 tiles, split 8 ways along F (100 steps: uneven ranges)
+    "split_single_round": dict(M=300, H=512, F=6400, E=4, k=2),
+    # ... with empty experts and ragged segments (128 steps)
+    "split_empty_experts": dict(M=200, H=256, F=8192, E=8, k=2, bias=[4, 4, 0, 0, -50, -50, 0, -50]),
     # held experts (expert-parallel share): a middle group, the last group with source blocks,
     # one held expert, and a held group nothing is routed to
     "local_mid": dict(M=300, H=256, F=320, E=16, k=4, base=4, local=4),

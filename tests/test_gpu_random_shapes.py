@@ -48,14 +48,16 @@ def _shape(i):
 MULTI = {
     # 2 segments of ~3000 rows (12 row tiles: cut into row blocks); Layer0
     # 24 x 18 = 432 tiles (1.7 rounds); Layer1 96 tiles split 2 ways along k
-    "tall_split2": dict(M=6000, H=1024, F=2304, E=2, k=1),
+    "tall_row_blocks": dict(M=6000, H=1024, F=2304, E=2, k=1),
     # Layer0 40 x 7 = 280 tiles: a last round of 24 tiles run as 48 halves
     "l0_halves": dict(M=5000, H=768, F=896, E=4, k=2),
     # Layer1 32 x 12 = 384 tiles: a last round of 128 tiles run as 256 halves
     "l1_halves": dict(M=4000, H=3072, F=512, E=2, k=2),
     # Layer0 32 x 32 = 1024 tiles (4 whole rounds); Layer1 32 x 10 = 320:
     # a last round of 64 tiles split 4 ways along k
-    "l1_split4": dict(M=4000, H=2560, F=4096, E=2, k=2),
+    "l0_whole_rounds": dict(M=4000, H=2560, F=4096, E=2, k=2),
+    # Layer1 28 x 12 = 336 tiles: a last round of 80 tiles split 3 ways along k
+    "l1_split3": dict(M=3500, H=3072, F=4736, E=2, k=2),
     # held experts 2..5 of 8, two source blocks: ~750-row segments
     "held_src_blocks": dict(M=6000, H=1024, F=1536, E=8, k=2, S=2, base=2, local=4),
     # 32 experts of ~375 rows: 64 x 6 = 384 Layer0 tiles, halves in the last round

@@ -29,6 +29,16 @@ size_t hact_bytes(const moe_problem_t* p, int64_t R) {
   return is_mx(p) ? (size_t)R * p->ffn + (size_t)mx_scale_bytes(R, p->ffn) : (size_t)R * p->ffn * elem_bytes(p);
 }
 
+// Whether the bf16 grouped GEMM combines each expert's segments of all the
+// source blocks into one: with source blocks whose (block, expert)
+// segments hold fewer rows than a tile on average (R EL / E kept pairs over
+// S EL segments, i.e. R / (E S) < 256), such as the expert-parallel share
+// that holds a few of many experts.
+bool combine_blocks(const moe_problem_t* p) {
+  return p->dtype == MOE_DTYPE_BF16 && p->num_src_blocks > 1 &&
+         p->num_tokens * p->topk < 256ll * p->num_experts * p->num_src_blocks;
+}
+
 // Experts held by the call (weights it is given): EL, or all E.
 int held(const moe_problem_t* p) { return p->local_experts > 0 ? p->local_experts : p->num_experts; }
 int held_base(const moe_problem_t* p) { return p->local_experts > 0 ? p->expert_base : 0; }
@@ -292,6 +302,7 @@ moe_status_t moe_grouped_gemm(const moe_problem_t* p, int32_t layer, const void*
   if (ws && !aligned(ws, 16)) return MOE_ERR_INVALID_ARGUMENT;
   gp.ws = ws;
   gp.ws_bytes = ws ? ws_bytes : 0;
+  gp.rowmap = combine_blocks(p);
   hipStream_t s = (hipStream_t)stream;
   if (debug_validate()) {
     st = validate_offsets(p, offsets, s);
@@ -450,6 +461,7 @@ moe_status_t moe_layer_ex(const moe_problem_t* p, const void* x, const float* lo
   gp.N = p->ffn;
   gp.ws = at<void>(ws, L.gemm);
   gp.ws_bytes = L.total - L.gemm;
+  gp.rowmap = combine_blocks(p);
   e = is_mx(p) ? launch_grouped_gemm_mx(gp, s)
               : (p->dtype == MOE_DTYPE_BF16 ? launch_grouped_gemm_bf16(gp, s) : launch_grouped_gemm_f32(gp, s));
   if (e != hipSuccess) return MOE_ERR_HIP;

@@ -88,10 +88,19 @@ __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirs
 //
 // OUT8 (layer 0): Hact is written as MXFP8 instead of bf16: e4m3 codes and,
 // per 32 columns of a token row, one scale byte (see mx_scale / e4m3_pack4).
-template <int LAYER, bool GATHER = false, int TM = kTileRows, bool PARTIAL = false, bool OUT8 = false>
+//
+// ROWMAP: the tile's token rows are not contiguous; rowpos[t] (LDS, t < TM)
+// holds the row (of a and of c) of tile row t, or -1 past the rows: a
+// segment made of the rows of several source blocks for one expert, whose
+// rows lie apart in the sorted order.  seg_rows and m0 then count the rows
+// of that combined segment, and seg_start is unused.
+template <int LAYER, bool GATHER = false, int TM = kTileRows, bool PARTIAL = false, bool OUT8 = false,
+          bool ROWMAP = false>
 __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int seg_start, int seg_rows, int m0,
                                                int nt, char* __restrict__ lds, int k0 = 0, int k1 = -1,
-                                               float* __restrict__ part = nullptr) {
+                                               float* __restrict__ part = nullptr,
+                                               const int* __restrict__ rowpos = nullptr) {
+  static_assert(!ROWMAP || (!GATHER && !PARTIAL && !OUT8), "row map: plain bf16 tiles");
   static_assert(TM == 256 || TM == 128, "token tile height");
   static_assert(!PARTIAL || (TM == 256 && LAYER == 1), "partial tiles: layer 1, full height");
   static_assert(!OUT8 || (LAYER == 0 && !PARTIAL), "MXFP8 output: layer 0");
@@ -139,6 +148,14 @@ __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int
       const int r = lr + 32 * i;
       xvoff[i] = 0x80000000u;
       if (r < trows) xvoff[i] = (uint32_t)(p.s2f[seg_start + m0 + r] / p.topk) * row_bytes + (uint32_t)lc * 16u;
+    }
+  } else if (ROWMAP) {
+    // rows of a at their own positions (p.M rows in all); -1 reads zeros
+    rx = make_rsrc(p.a, (uint32_t)(p.M * (int64_t)row_bytes));
+#pragma unroll
+    for (int i = 0; i < XI; ++i) {
+      const int r = rowpos[lr + 32 * i];
+      xvoff[i] = r >= 0 ? (uint32_t)r * row_bytes + (uint32_t)lc * 16u : 0x80000000u;
     }
   } else {
     rx = make_rsrc(p.a + (int64_t)(seg_start + m0) * K, (uint32_t)trows * row_bytes);
@@ -504,7 +521,7 @@ __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int
       if (t & 1) v = i32x4_t{v[2], v[3], v[0], v[1]};
       const int trow = m0 + t;
       if (trow < seg_rows && f < N)
-        *reinterpret_cast<i32x4_t*>(hact + (int64_t)(seg_start + trow) * N + f) = v;
+        *reinterpret_cast<i32x4_t*>(hact + (int64_t)(ROWMAP ? rowpos[t] : seg_start + trow) * N + f) = v;
     }
     __syncthreads();
   } else {
@@ -540,8 +557,10 @@ __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int
 #pragma unroll 4
       for (int ts = tid >> 6; ts < 128; ts += kGemmThreads / 64) {
         const f32x4_t v = *reinterpret_cast<const f32x4_t*>(stg + ts * 1024 + ((c ^ (ts & 15)) << 4));
-        const int trow = m0 + (ts >> 6) * (TM / 2) + 64 * P + (ts & 63);
-        if (trow < seg_rows && n < N) *reinterpret_cast<f32x4_t*>(y + (int64_t)(seg_start + trow) * N + n) = v;
+        const int t = (ts >> 6) * (TM / 2) + 64 * P + (ts & 63);
+        const int trow = m0 + t;
+        if (trow < seg_rows && n < N)
+          *reinterpret_cast<f32x4_t*>(y + (int64_t)(ROWMAP ? rowpos[t] : seg_start + trow) * N + n) = v;
       }
       __syncthreads();
     }
@@ -555,13 +574,16 @@ __device__ __forceinline__ void bf16_gemm_tile(const Bf16GemmArgs& p, int g, int
 // running at once on an XCD stay in step and share the segment's weight
 // panels in its L2 (measured: halving those last tiles cost more in
 // re-read weights than it saved).
-template <int LAYER, bool GATHER = false, bool OUT8 = false>
+template <int LAYER, bool GATHER = false, bool OUT8 = false, bool ROWMAP = false>
 __device__ __forceinline__ void bf16_gemm_row_tile(const Bf16GemmArgs& p, int g, int seg_start, int seg_rows, int m0,
-                                                   int nt, char* __restrict__ lds) {
+                                                   int nt, char* __restrict__ lds,
+                                                   const int* __restrict__ rowpos = nullptr) {
   if (seg_rows <= kTileRows / 2)
-    bf16_gemm_tile<LAYER, GATHER, kTileRows / 2, false, OUT8>(p, g, seg_start, seg_rows, m0, nt, lds);
+    bf16_gemm_tile<LAYER, GATHER, kTileRows / 2, false, OUT8, ROWMAP>(p, g, seg_start, seg_rows, m0, nt, lds, 0, -1,
+                                                                      nullptr, rowpos);
   else
-    bf16_gemm_tile<LAYER, GATHER, kTileRows, false, OUT8>(p, g, seg_start, seg_rows, m0, nt, lds);
+    bf16_gemm_tile<LAYER, GATHER, kTileRows, false, OUT8, ROWMAP>(p, g, seg_start, seg_rows, m0, nt, lds, 0, -1,
+                                                                  nullptr, rowpos);
 }
 
 }  // namespace moe

@@ -116,6 +116,49 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(Bf16Gem
   }
 }
 
+// The grouped GEMM over combined per-expert segments (GemmProblem::rowmap):
+// when the rows arrive in many source blocks, the segment of one (source
+// block, expert) pair can be far shorter than a tile (the expert-parallel
+// share that holds 16 of 128 experts: about 128 rows each), so every
+// weight panel would be streamed once per source block for half a tile of
+// rows.  Here the S segments of expert e are one combined segment
+// (build_expert_tile_table), and each tile looks up its rows' sorted
+// positions once (expert_row, into LDS) for its loads and its stores.  The
+// same static schedule and last-round halves as the kernel above; no split
+// along k.  Every element is computed as in any other tile, so the bits do
+// not change.
+template <int LAYER>
+__global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_expert_kernel(Bf16GemmArgs args,
+                                                                                const int32_t* __restrict__ offsets,
+                                                                                int G, int xcd_slots) {
+  __shared__ __attribute__((aligned(16))) char lds[kGemmLdsBytes];
+  __shared__ TileLds tl;
+  __shared__ int rowpos[kTileRows];
+  const int EL = args.E, S = G / EL;
+  const int NT = (args.N + (LAYER == 0 ? kL0Cols : kL1Cols) - 1) / (LAYER == 0 ? kL0Cols : kL1Cols);
+  const int T = build_expert_tile_table(offsets, G, EL, kTileRows, tl) * NT;
+  const int64_t rtb = (int64_t)kTileRows * args.K * 2;
+  const int grid = gridDim.x;
+  const int r = T % grid;
+  const int half = (r > 0 && 2 * r <= grid && T > grid) ? r : 0;  // tiles of the last round to halve
+  const int entries = T + half;
+  for (int v = xcd_slot(blockIdx.x, grid); v < entries; v += grid) {
+    const bool is_half = v >= T - half;
+    const int j = v - (T - half);
+    const TileCoord c = tile_coord(is_half ? T - half + j / 2 : v, EL, NT, kTileRows, xcd_slots, rtb, tl);
+    const int m0 = is_half ? c.m0 + (j & 1) * (kTileRows / 2) : c.m0;
+    const int n = tl.expert_rows[c.g];
+    if (m0 >= n) continue;
+    rowpos[threadIdx.x] = expert_row(tl, c.g, EL, S, m0, threadIdx.x);
+    __syncthreads();
+    if (is_half)
+      bf16_gemm_tile<LAYER, false, kTileRows / 2, false, false, true>(args, c.g, 0, n, m0, c.nt, lds, 0, -1, nullptr,
+                                                                      rowpos);
+    else
+      bf16_gemm_row_tile<LAYER, false, false, true>(args, c.g, 0, n, m0, c.nt, lds, rowpos);
+  }
+}
+
 // Layer1 on MXFP8 operands: the same persistent schedule (tile order,
 // half-height tiles for single-tile segments of at most 128 rows and for a
 // last round that would leave more than half the CUs idle) with the MXFP8
@@ -347,6 +390,14 @@ hipError_t launch_grouped_gemm_bf16(const GemmProblem& gp, hipStream_t s) {
   a.a_scale_bytes = a.w_scale_bytes = 0;
   const int grid = device_cu_count();
   const int xcd_slots = grid / kXcds > 0 ? grid / kXcds : 1;
+  if (gp.rowmap) {
+    a.M = gp.R;  // rows of the token-row buffer, read at their own positions
+    if (gp.layer == 0)
+      grouped_gemm_bf16_expert_kernel<0><<<grid, kGemmThreads, 0, s>>>(a, gp.offsets, gp.G, xcd_slots);
+    else
+      grouped_gemm_bf16_expert_kernel<1><<<grid, kGemmThreads, 0, s>>>(a, gp.offsets, gp.G, xcd_slots);
+    return hipGetLastError();
+  }
   SplitWs sp{nullptr, nullptr, nullptr};
   // layer 1 only; the header holds descriptors of up to 4096 split tiles (fewer than the grid)
   if (gp.layer == 1 && gp.ws && gp.ws_bytes >= gemm_split_ws_bytes() && grid <= 4096) {

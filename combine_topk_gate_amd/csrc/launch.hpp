@@ -57,6 +57,7 @@ struct GemmProblem {
   int G;
   void* ws = nullptr;       // bf16: split workspace of gemm_split_ws_bytes(), or null
   size_t ws_bytes = 0;
+  int rowmap = 0;           // bf16: each expert's segments of all source blocks as one (G / E of them)
 };
 // Workspace that lets the bf16 grouped GEMM split its last round along K.
 size_t gemm_split_ws_bytes();

@@ -30,6 +30,7 @@ struct TileLds {
   int seg_rows[kMaxTileSegs + 1];
   int mt_start[kMaxTileSegs + 1];
   int scratch[256];
+  int expert_rows[kMaxTileSegs / 2 + 1];  // rows of each expert over all source blocks (row-map tables)
 };
 
 // Fills seg_start, seg_rows and mt_start from offsets; returns the number of
@@ -62,6 +63,63 @@ __device__ inline int build_tile_table(const int32_t* __restrict__ offsets, int 
   if (threadIdx.x == 0) t.mt_start[G] = total;
   __syncthreads();
   return total;
+}
+
+// The table of a grouped GEMM whose segments are S = G / EL source blocks of
+// EL experts each (segment g = s EL + e): each expert's rows, over all its
+// source blocks, form one combined segment, so a tile of 256 rows can take
+// rows of several small segments of the same expert and every weight panel
+// serves full tiles.  Fills seg_start and seg_rows of the G segments,
+// expert_rows[e] and mt_start[e] (prefix of the experts' M-tile counts);
+// returns the number of M-tiles.  All threads of the block (<= 256) call it.
+__device__ inline int build_expert_tile_table(const int32_t* __restrict__ offsets, int G, int EL, int rows,
+                                              TileLds& t) {
+  const int nthr = blockDim.x;
+  for (int g = threadIdx.x; g < G; g += nthr) {
+    t.seg_start[g] = offsets[g];
+    t.seg_rows[g] = offsets[g + 1] - offsets[g];
+  }
+  __syncthreads();
+  const int S = G / EL;
+  const int per = (EL + nthr - 1) / nthr;
+  const int e0 = threadIdx.x * per;
+  int run = 0;
+  for (int e = e0; e < e0 + per && e < EL; ++e) {
+    int n = 0;
+    for (int s = 0; s < S; ++s) n += t.seg_rows[s * EL + e];
+    t.expert_rows[e] = n;
+    run += (n + rows - 1) / rows;
+  }
+  t.scratch[threadIdx.x] = run;
+  __syncthreads();
+  for (int off = 1; off < nthr; off <<= 1) {
+    const int v = (threadIdx.x >= (unsigned)off) ? t.scratch[threadIdx.x - off] : 0;
+    __syncthreads();
+    t.scratch[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int acc = t.scratch[threadIdx.x] - run;
+  for (int e = e0; e < e0 + per && e < EL; ++e) {
+    t.mt_start[e] = acc;
+    acc += (t.expert_rows[e] + rows - 1) / rows;
+  }
+  const int total = t.scratch[nthr - 1];
+  if (threadIdx.x == 0) t.mt_start[EL] = total;
+  __syncthreads();
+  return total;
+}
+
+// Sorted row of row m0 + i (i < n) of expert e's combined segment, -1 past
+// its rows: the source blocks' segments in order.
+__device__ inline int expert_row(const TileLds& t, int e, int EL, int S, int m0, int i) {
+  int r = m0 + i;
+  if (r >= t.expert_rows[e]) return -1;
+  for (int s = 0; s < S; ++s) {
+    const int n = t.seg_rows[s * EL + e];
+    if (r < n) return t.seg_start[s * EL + e] + r;
+    r -= n;
+  }
+  return -1;
 }
 
 // Last segment g with mt_start[g] * mult <= v (v below the total).

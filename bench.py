@@ -52,6 +52,9 @@ def parse():
                     help="skip the context line: this GEMM and torch.matmul (hipBLASLt) on one dense expert")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (to scale the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the layer step and the chain (no epilogue, cold-cache, fused or dense "
+                         "context measurements): for profiler runs")
     return ap.parse_args()
 
 
@@ -299,17 +302,25 @@ def main():
         moe.moe_combine_ex(p, y, w, f2s, epi, out_bf16, stream)
         if ev: ev[1].record(stream)
 
-    _, per_epi = time_steps(step_epilogue, 2, args.warmup, args.steps)
+    per_epi = np.array([[np.nan]])
+    if not args.no_extras:
+        _, per_epi = time_steps(step_epilogue, 2, args.warmup, args.steps)
 
-    # (4) cold cache: dispatch and combine alone, a 1 GiB scrub written
-    #     between repetitions (the 256 MB last-level cache then holds
-    #     nothing of their inputs); only the call itself is timed
+    # (4) cold cache: dispatch and combine alone with a 1 GiB scrub between
+    #     repetitions, so the 256 MB last-level cache holds nothing of their
+    #     inputs; only the call itself is timed.  The scrub is written (the
+    #     cache is then full of dirty lines that must be written back as the
+    #     call evicts them) or read (clean lines)
     scrub = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    scrub32 = scrub.view(torch.float32)
 
-    def cold(fn, reps):
+    def cold(fn, reps, mode="write"):
         ts = []
         for i in range(reps + 2):
-            scrub.fill_(i & 0xFF)
+            if mode == "write":
+                scrub.fill_(i & 0xFF)
+            else:
+                float(scrub32.sum())
             a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a_.record(stream)
             fn()
@@ -319,15 +330,20 @@ def main():
                 ts.append(a_.elapsed_time(b_) * 1e3)
         return np.array(ts)
 
-    cold_disp = cold(lambda: moe.moe_dispatch(p, g["x"], idx, src, counts, offsets, s2f, f2s, xp, ws_d, stream),
-                     args.steps)
-    cold_comb = cold(lambda: moe.moe_combine(p, y, w, f2s, out, stream), args.steps)
-    del scrub
+    cold_t = {}
+    if not args.no_extras:
+        scrub.zero_()
+        for mode in ("write", "read"):
+            cold_t[mode] = {
+                "dispatch": cold(lambda: moe.moe_dispatch(p, g["x"], idx, src, counts, offsets, s2f, f2s, xp, ws_d,
+                                                          stream), args.steps, mode),
+                "combine": cold(lambda: moe.moe_combine(p, y, w, f2s, out, stream), args.steps, mode)}
+    del scrub, scrub32
 
     # (5) the fused kernel at this shape (whatever the table picks for the
     #     step above): shared queue, and 8 dedicated combine workgroups
     fused_us = {}
-    if cfg.dtype == "bf16":
+    if cfg.dtype == "bf16" and not args.no_extras:
         for nm in (0, 8):
             def step_fused(ev, nm=nm):
                 if ev: ev[0].record(stream)
@@ -376,17 +392,21 @@ def main():
     disp_bytes = Tk * H * eb + Rk * H * eb + R * 4
     comb_bytes = Rk * H * 4 + M * H * 4 + M * k * 8
     epi_bytes = Rk * H * 4 + M * H * eb + M * H * 2 + M * k * 8
-    res["combine_epilogue_us"] = float(per_epi.mean())
-    res["combine_epilogue_gbs"] = epi_bytes / (per_epi.mean() * 1e-6) / 1e9
+    if not args.no_extras:
+        res["combine_epilogue_us"] = float(per_epi.mean())
+        res["combine_epilogue_gbs"] = epi_bytes / (per_epi.mean() * 1e-6) / 1e9
     res["dispatch_gbs"] = disp_bytes / (mean[1] * 1e-6) / 1e9
     res["combine_gbs"] = comb_bytes / (mean[4] * 1e-6) / 1e9
     res["dispatch_pct_hbm"] = 100.0 * res["dispatch_gbs"] / PEAK_HBM_GBS
     res["combine_pct_hbm"] = 100.0 * res["combine_gbs"] / PEAK_HBM_GBS
     # the same two calls timed alone after a 1 GiB scrub (cold last-level cache)
-    res["cold_us_p10_p50_p90"] = {"dispatch": [float(np.percentile(cold_disp, q)) for q in (10, 50, 90)],
-                                  "combine": [float(np.percentile(cold_comb, q)) for q in (10, 50, 90)]}
-    res["dispatch_cold_pct_hbm"] = 100.0 * disp_bytes / (np.median(cold_disp) * 1e-6) / 1e9 / PEAK_HBM_GBS
-    res["combine_cold_pct_hbm"] = 100.0 * comb_bytes / (np.median(cold_comb) * 1e-6) / 1e9 / PEAK_HBM_GBS
+    for mode, tt in cold_t.items():
+        res[f"cold_{mode}_scrub_us_p10_p50_p90"] = {k_: [float(np.percentile(v_, q)) for q in (10, 50, 90)]
+                                                   for k_, v_ in tt.items()}
+        res[f"dispatch_cold_{mode}_scrub_pct_hbm"] = (100.0 * disp_bytes / (np.median(tt["dispatch"]) * 1e-6) / 1e9
+                                                     / PEAK_HBM_GBS)
+        res[f"combine_cold_{mode}_scrub_pct_hbm"] = (100.0 * comb_bytes / (np.median(tt["combine"]) * 1e-6) / 1e9
+                                                    / PEAK_HBM_GBS)
     # single-GPU analogue of hidden communication (the pages' share of
     # communication hidden): 1 - (fused - route - L0 - L1) / (dispatch +
     # combine), with the chain's step times; negative when the fused kernel
@@ -408,7 +428,7 @@ def main():
                                         "reads the 256 MB last-level cache serves are included",
                        "launch_us": float(mean[2]),
                        "algorithmic": f"4*R*H*F = {l0_flops:.4g} flop per launch"}
-    if cfg.dtype == "bf16" and not args.no_dense_ref:
+    if cfg.dtype == "bf16" and not args.no_dense_ref and not args.no_extras:
         res["context_dense_same_shape"] = dense_reference(moe, R, H, F)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, d, args.cpu_seconds)

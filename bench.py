@@ -420,7 +420,12 @@ def main():
         res["movement_hidden_pct"] = None
     l0_flops = 4.0 * Rk * H * F
     ach = l0_flops / (mean[2] * 1e-6) / 1e12
-    res["roofline"] = {"kernel": "grouped_gemm_bf16_kernel<0> (Layer0 gate/up + SwiGLU), chain timing",
+    # bf16 rows from several source blocks whose (block, expert) segments
+    # average under one 256-row tile run the kernel over combined per-expert
+    # segments (the library's rule, api.hip combine_blocks)
+    rowmap = cfg.dtype == "bf16" and cfg.S > 1 and cfg.M * cfg.k < 256 * cfg.E * cfg.S
+    l0_kernel = "grouped_gemm_bf16_expert_kernel<0>" if rowmap else "grouped_gemm_bf16_kernel<0>"
+    res["roofline"] = {"kernel": f"{l0_kernel} (Layer0 gate/up + SwiGLU), chain timing",
                        "bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak,
                        "traffic": measured_traffic("grouped_gemm_bf16_kernel<0>") if cfg.name == "mixtral" else None,
                        "traffic_scope": "bytes between the XCDs' L2 caches and the memory fabric per launch "

@@ -341,17 +341,18 @@ def main():
     del scrub, scrub32
 
     # (5) the fused kernel at this shape (whatever the table picks for the
-    #     step above): shared queue, and 8 dedicated combine workgroups
+    #     step above): shared queue, 8 dedicated combine workgroups, and the
+    #     shared queue with Layer0 reading the dispatch's X_perm copy
     fused_us = {}
     if cfg.dtype == "bf16" and not args.no_extras:
-        for nm in (0, 8):
-            def step_fused(ev, nm=nm):
+        for nm, ga in ((0, 1), (8, 1), (0, 0)):
+            def step_fused(ev, nm=nm, ga=ga):
                 if ev: ev[0].record(stream)
                 moe.moe_layer(p, g["x"], g["logits"], src, g["w_gate"], g["w_up"], w_down, out, ws_l,
-                              n_mover=nm, fused=1, stream=stream)
+                              n_mover=nm, fused=1, gather=ga, stream=stream)
                 if ev: ev[1].record(stream)
             ms_f, _ = time_steps(step_fused, 2, 2, max(3, args.steps // 4))
-            fused_us[f"n_mover={nm}"] = ms_f * 1e3
+            fused_us[f"n_mover={nm}" + ("" if ga else ",copy")] = ms_f * 1e3
 
     # pairs routed to held experts (all of them unless only some are held)
     Rk = int(offsets[-1].item())

@@ -66,7 +66,7 @@ class LayerAux(ctypes.Structure):
 
 class LayerOpts(ctypes.Structure):
     _fields_ = [("n_mover", ctypes.c_int32), ("grid", ctypes.c_int32), ("fused", ctypes.c_int32),
-                ("spin_limit", ctypes.c_int32)]
+                ("spin_limit", ctypes.c_int32), ("gather", ctypes.c_int32)]
 
 
 _lib = None
@@ -222,22 +222,24 @@ def moe_quantize_mxfp8(src, dst, stream=None):
 
 
 def moe_layer(p, x, logits, src_block, w_gate, w_up, w_down, out, ws, aux: dict | None = None,
-              n_mover: int = -1, grid: int = 0, fused: int = 1, spin_limit: int = 0, stream=None):
+              n_mover: int = -1, grid: int = 0, fused: int = 1, spin_limit: int = 0,
+              gather: int = -1, stream=None):
     a = None
     if aux:
         a = LayerAux(**{k: (v.data_ptr() if v is not None else None) for k, v in aux.items()})
-    o = LayerOpts(int(n_mover), int(grid), int(fused), int(spin_limit))
+    o = LayerOpts(int(n_mover), int(grid), int(fused), int(spin_limit), int(gather))
     _check(load_library().moe_layer(ctypes.byref(p), _ptr(x), _ptr(logits), _ptr(src_block), _ptr(w_gate),
                                     _ptr(w_up), _ptr(w_down), _ptr(out), ctypes.byref(a) if a else None,
                                     ctypes.byref(o), _ptr(ws), _nbytes(ws), _stream(stream)), "moe_layer")
 
 
 def moe_layer_ex(p, x, logits, src_block, w_gate, w_up, w_down, epi, out, ws, aux: dict | None = None,
-                 n_mover: int = -1, grid: int = 0, fused: int = 1, spin_limit: int = 0, stream=None):
+                 n_mover: int = -1, grid: int = 0, fused: int = 1, spin_limit: int = 0,
+              gather: int = -1, stream=None):
     a = None
     if aux:
         a = LayerAux(**{k: (v.data_ptr() if v is not None else None) for k, v in aux.items()})
-    o = LayerOpts(int(n_mover), int(grid), int(fused), int(spin_limit))
+    o = LayerOpts(int(n_mover), int(grid), int(fused), int(spin_limit), int(gather))
     _check(load_library().moe_layer_ex(ctypes.byref(p), _ptr(x), _ptr(logits), _ptr(src_block), _ptr(w_gate),
                                        _ptr(w_up), _ptr(w_down), ctypes.byref(epi) if epi is not None else None,
                                        _ptr(out), ctypes.byref(a) if a else None, ctypes.byref(o), _ptr(ws),

@@ -385,6 +385,7 @@ moe_status_t moe_layer_ex(const moe_problem_t* p, const void* x, const float* lo
   o.grid = 0;
   o.fused = 1;
   o.spin_limit = 0;
+  o.gather = -1;
   if (opts) o = *opts;
 
   if (debug_validate() && M > 0) {
@@ -419,6 +420,10 @@ moe_status_t moe_layer_ex(const moe_problem_t* p, const void* x, const float* lo
     fa.k = p->topk;
     fa.G = G;
     fa.x = x;
+    // Layer0 gathers its token rows from x unless the caller asks for the
+    // X_perm copy (o.gather == 0)
+    const bool gather = o.gather != 0;
+    fa.x_perm = gather ? nullptr : xp;
     fa.w_gate = w_gate;
     fa.w_up = w_up;
     fa.w_down = w_down;
@@ -437,10 +442,10 @@ moe_status_t moe_layer_ex(const moe_problem_t* p, const void* x, const float* lo
     fa.spin_limit = o.spin_limit;
     moe_status_t fs = fused_check(fa, cus);
     if (fs != MOE_OK) return fs;
-    // the fused kernel reads token rows straight from x; X_perm is produced
-    // only when the caller asks for it
+    // gathering, the kernel reads token rows straight from x and X_perm is
+    // produced only when the caller asks for it
     e = launch_dispatch(plan_of(p), idx, src, counts, offsets, s2f, f2s, x, (int64_t)p->hidden * elem_bytes(p),
-                        a.x_perm ? xp : nullptr, at<int32_t>(ws, L.perm), s);
+                        (!gather || a.x_perm) ? xp : nullptr, at<int32_t>(ws, L.perm), s);
     if (e != hipSuccess) return MOE_ERR_HIP;
     return hip_status(launch_fused_layer(fa, s));
   }

@@ -14,10 +14,12 @@
 // On one GPU the pages' communication becomes HBM traffic: the gather of
 // token rows and the scatter-reduce of expert outputs.  A handful of
 // workgroups cannot drive HBM (a copy needs many CUs' worth of loads in
-// flight), so the gather is not a separate stage here: Layer0 tiles read
-// their token rows straight from x through sorted_to_flat (the GEMM loads
-// the rows anyway), and X_perm is never written.  What remains is the
-// combine, which runs on workgroups chosen in one of two ways:
+// flight), so the gather is not a stage of this kernel: by default Layer0
+// tiles read their token rows straight from x through sorted_to_flat (the
+// GEMM loads the rows anyway) and X_perm is not written; with x_perm set,
+// the dispatch has copied them and the tiles read X_perm as in the chain.
+// What remains is the combine, which runs on workgroups chosen in one of
+// two ways:
 //   n_mover > 0  workgroups [0, n_mover) are dedicated combiners: they take
 //                combine items (column chunk c, block of 32 tokens) in
 //                order, each as soon as chunk c's Layer1 tiles are done;
@@ -229,13 +231,18 @@ __global__ __launch_bounds__(kGemmThreads) void fused_layer_kernel(FusedArgs a) 
     if (v >= total) return;
     if (v < T0) {
       const TileCoord c = tile_coord(v, a.G, nt0, kTileRows, xcd_slots, (int64_t)kTileRows * a.H * 2, tl);
-      ga.a = reinterpret_cast<const __bf16*>(a.x);
       ga.w0 = reinterpret_cast<const __bf16*>(a.w_gate);
       ga.w1 = reinterpret_cast<const __bf16*>(a.w_up);
       ga.c = a.hact;
       ga.K = a.H;
       ga.N = a.F;
-      bf16_gemm_row_tile<0, true>(ga, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], c.m0, c.nt, lds);
+      if (a.x_perm) {
+        ga.a = reinterpret_cast<const __bf16*>(a.x_perm);
+        bf16_gemm_row_tile<0>(ga, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], c.m0, c.nt, lds);
+      } else {
+        ga.a = reinterpret_cast<const __bf16*>(a.x);
+        bf16_gemm_row_tile<0, true>(ga, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], c.m0, c.nt, lds);
+      }
       block_signal(l0done + c.mt, 1);
       continue;
     }

@@ -15,6 +15,7 @@ struct FusedArgs {
   int64_t M;
   int H, F, E, k, G;
   const void* x;
+  const void* x_perm;  // non-null: Layer0 reads X_perm (written by the dispatch); null: it gathers from x
   const void* w_gate;
   const void* w_up;
   const void* w_down;

@@ -278,15 +278,20 @@ typedef struct {
   int32_t grid;        /* total persistent workgroups; <=0: every CU, one each */
   int32_t fused;       /* 0: run the unfused kernel chain instead of the fused kernel */
   int32_t spin_limit;  /* >0: bound on each device wait (polls); 0: default bound */
+  int32_t gather;      /* Layer0's token rows in the fused kernel: 1 or <0 (default): read straight
+                          from x through sorted_to_flat (X_perm not written unless aux->x_perm is
+                          given); 0: the dispatch writes X_perm and Layer0 reads it, as in the chain
+                          (measured: 1% faster at Mixtral's shape, 1-2% slower at the others) */
 } moe_layer_opts_t;
 
 /*
  * The whole layer ([COMET] §4.2.1 thread-block specialisation, §4.2.2
  * adaptive allocation, §4.1.1-§4.1.2 shared-tensor decomposition and
  * column-wise Layer1; [PTO] MegaMoE seven-stage fusion, ready counters,
- * dynamic core grouping): route, dispatch bookkeeping, then one persistent
- * kernel (bf16 layers) whose workgroups take, from one ordered queue,
- * Layer0 tiles (token rows read straight from x through sorted_to_flat),
+ * dynamic core grouping): route, dispatch (the X_perm copy only with
+ * opts->gather = 0), then one persistent kernel (bf16 layers) whose
+ * workgroups take, from one ordered queue, Layer0 tiles (token rows read
+ * straight from x through sorted_to_flat, or from X_perm with gather = 0),
  * Layer1 tiles column chunk by column chunk (each once its row tile's
  * Layer0 tiles are done), and combine items (a column chunk of a block of
  * tokens, once that chunk's Layer1 tiles are done) -- either on n_mover
@@ -300,7 +305,8 @@ typedef struct {
  *   x [M,H] dtype; logits [M,E] f32; src_block [M] int32 or NULL (S = 1);
  *   w_gate, w_up [EL,F,H]; w_down [EL,H,F]; out [M,H] f32 (the partial
  *   combine when EL < E).
- *   aux: the fused path writes X_perm only if aux->x_perm is given.
+ *   aux: gathering, the fused path writes X_perm only if aux->x_perm is
+ *   given.
  * The fused kernel needs its whole grid resident (one workgroup per CU):
  * opts->grid above that returns MOE_ERR_UNSUPPORTED; n_mover >= grid returns
  * MOE_ERR_INVALID_ARGUMENT.  If a bounded device wait runs out, the kernel

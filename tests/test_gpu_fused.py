@@ -41,26 +41,29 @@ def ep():
     return _case(moe_synth.Config("ep2k", 2048, 1024, 512, 16, 8, 8, "bf16", 32, 0.0, 256))
 
 
+@pytest.mark.parametrize("gather", [0, 1])
 @pytest.mark.parametrize("n_mover", [0, 1, 2, 8, 32, 64])
-def test_schedule_invariance_movers(qwen, n_mover):
+def test_schedule_invariance_movers(qwen, n_mover, gather):
     cfg, g, chain = qwen
-    out, _, status = run_layer(cfg, g, n_mover=n_mover)
+    out, _, status = run_layer(cfg, g, n_mover=n_mover, gather=gather)
     assert status == moe.MOE_OK
     assert torch.equal(out, chain["out"])
 
 
-@pytest.mark.parametrize("grid,n_mover", [(7, 0), (16, 2), (64, 8), (200, 3), (256, 0), (256, 16)])
-def test_schedule_invariance_grid(mix, grid, n_mover):
+@pytest.mark.parametrize("grid,n_mover,gather", [(7, 0, 0), (16, 2, 1), (64, 8, 0), (200, 3, 1), (256, 0, 0),
+                                                 (256, 0, 1), (256, 16, 0)])
+def test_schedule_invariance_grid(mix, grid, n_mover, gather):
     cfg, g, chain = mix
-    out, _, status = run_layer(cfg, g, n_mover=n_mover, grid=grid)
+    out, _, status = run_layer(cfg, g, n_mover=n_mover, grid=grid, gather=gather)
     assert status == moe.MOE_OK
     assert torch.equal(out, chain["out"])
 
 
+@pytest.mark.parametrize("gather", [0, 1])
 @pytest.mark.parametrize("n_mover", [0, 8])
-def test_source_blocks(ep, n_mover):
+def test_source_blocks(ep, n_mover, gather):
     cfg, g, chain = ep
-    out, _, status = run_layer(cfg, g, n_mover=n_mover)
+    out, _, status = run_layer(cfg, g, n_mover=n_mover, gather=gather)
     assert status == moe.MOE_OK
     assert torch.equal(out, chain["out"])
 
@@ -75,6 +78,21 @@ def test_intermediates_equal_chain(qwen):
     for key in ("topk_idx", "topk_w", "counts", "offsets", "sorted_to_flat", "flat_to_sorted", "y"):
         assert torch.equal(aux[key], chain[key]), key
     for key in ("x_perm", "hact"):
+        assert torch.equal(aux[key].view(torch.int16), chain[key].view(torch.int16)), key
+    assert torch.equal(out, chain["out"])
+
+
+@pytest.mark.parametrize("gather", [0, 1])
+def test_fused_intermediates_equal_unsplit_chain(qwen, gather):
+    # forced fused: X_perm (written by the dispatch unless gathering), Hact
+    # and Y bit for bit those of the chain without a grouped-GEMM workspace
+    cfg, g, chain = qwen
+    out, aux, status = run_layer(cfg, g, aux=True, n_mover=0, gather=gather)
+    assert status == moe.MOE_OK
+    for key in ("topk_idx", "topk_w", "counts", "offsets", "sorted_to_flat", "flat_to_sorted", "y"):
+        assert torch.equal(aux[key], chain[key]), key
+    for key in ("x_perm", "hact"):
+        # aux given: the gathering path writes X_perm too
         assert torch.equal(aux[key].view(torch.int16), chain[key].view(torch.int16)), key
     assert torch.equal(out, chain["out"])
 

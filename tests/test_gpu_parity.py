@@ -98,23 +98,26 @@ def test_layer_equals_chain_bitwise(case):
     assert torch.equal(out, ref["out"])
 
 
-@pytest.mark.parametrize("n_mover", [0, 8])
-def test_fused_layer_against_oracle(case, n_mover):
-    """The fused kernel (token rows gathered in Layer0's loads, one ordered
-    queue, ready counters) at the full shape, against the oracle directly:
-    its Hact and Y on the tile-covering rows and its output on the token
-    sample; and bitwise against the unsplit chain."""
+@pytest.mark.parametrize("n_mover,gather", [(0, 0), (8, 0), (0, 1), (8, 1)])
+def test_fused_layer_against_oracle(case, n_mover, gather):
+    """The fused kernel (Layer0 reading X_perm, or with gather = 1 the token
+    rows straight from x; one ordered queue, ready counters) at the full
+    shape, against the oracle directly: its Hact and Y on the tile-covering
+    rows and its output on the token sample; and bitwise against the
+    unsplit chain."""
     c = case
     if c["cfg"].dtype != "bf16":
         pytest.skip("the fused kernel runs bf16 layers")
-    out, aux, status = run_layer(c["cfg"], c["g"], aux=True, n_mover=n_mover)
+    out, aux, status = run_layer(c["cfg"], c["g"], aux=True, n_mover=n_mover, gather=gather)
     assert status == 0
     n = kept_rows(aux)
     assert n == int(c["ref"]["offsets"][-1])
-    for key in ("hact", "y"):
+    keys = ("hact", "y") if gather else ("x_perm", "hact", "y")
+    for key in keys:
         assert bool(torch.isfinite(aux[key][:n]).all()), key
-    tp.check_ffn(c, aux, f"fused n_mover={n_mover}")
-    tp.check_out(c, aux, out, f"fused n_mover={n_mover}")
+    name = f"fused n_mover={n_mover} gather={gather}"
+    tp.check_ffn(c, aux, name)
+    tp.check_out(c, aux, out, name)
     un = run_chain(c["cfg"], c["g"], gemm_ws=False)
     assert torch.equal(out, un["out"])
 

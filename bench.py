@@ -425,7 +425,8 @@ def main():
     # average under one 256-row tile run the kernel over combined per-expert
     # segments (the library's rule, api.hip combine_blocks)
     rowmap = cfg.dtype == "bf16" and cfg.S > 1 and cfg.M * cfg.k < 256 * cfg.E * cfg.S
-    l0_kernel = "grouped_gemm_bf16_expert_kernel<0>" if rowmap else "grouped_gemm_bf16_kernel<0>"
+    l0_kernel = ("grouped_gemm_f32_kernel<0>" if cfg.dtype == "f32" else
+                 "grouped_gemm_bf16_expert_kernel<0>" if rowmap else "grouped_gemm_bf16_kernel<0>")
     res["roofline"] = {"kernel": f"{l0_kernel} (Layer0 gate/up + SwiGLU), chain timing",
                        "bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak,
                        "traffic": measured_traffic("grouped_gemm_bf16_kernel<0>") if cfg.name == "mixtral" else None,

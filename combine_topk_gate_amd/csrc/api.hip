@@ -105,6 +105,20 @@ bool debug_validate() {
   return v && v[0] == '1' && v[1] == 0;
 }
 
+// MOE_DEBUG_SHUFFLE=<n>: the seed of the reordering check (0 or unset: the
+// usual order; anything but a decimal number below 2^32 counts as unset).
+uint32_t debug_shuffle() {
+  const char* v = getenv("MOE_DEBUG_SHUFFLE");
+  if (!v || !*v) return 0;
+  uint64_t n = 0;
+  for (const char* c = v; *c; ++c) {
+    if (*c < '0' || *c > '9') return 0;
+    n = n * 10 + (uint64_t)(*c - '0');
+    if (n > 0xffffffffull) return 0;
+  }
+  return (uint32_t)n;
+}
+
 template <typename T>
 bool fetch(std::vector<T>& h, const T* d, int64_t n, hipStream_t s) {
   h.resize(n > 0 ? (size_t)n : 0);
@@ -303,6 +317,7 @@ moe_status_t moe_grouped_gemm(const moe_problem_t* p, int32_t layer, const void*
   gp.ws = ws;
   gp.ws_bytes = ws ? ws_bytes : 0;
   gp.rowmap = combine_blocks(p);
+  gp.shuffle = debug_shuffle();
   hipStream_t s = (hipStream_t)stream;
   if (debug_validate()) {
     st = validate_offsets(p, offsets, s);
@@ -440,6 +455,7 @@ moe_status_t moe_layer_ex(const moe_problem_t* p, const void* x, const float* lo
     fa.grid = o.grid > 0 ? o.grid : cus;
     fa.n_mover = movers;
     fa.spin_limit = o.spin_limit;
+    fa.shuffle = debug_shuffle();
     moe_status_t fs = fused_check(fa, cus);
     if (fs != MOE_OK) return fs;
     // gathering, the kernel reads token rows straight from x and X_perm is
@@ -467,6 +483,7 @@ moe_status_t moe_layer_ex(const moe_problem_t* p, const void* x, const float* lo
   gp.ws = at<void>(ws, L.gemm);
   gp.ws_bytes = L.total - L.gemm;
   gp.rowmap = combine_blocks(p);
+  gp.shuffle = debug_shuffle();
   e = is_mx(p) ? launch_grouped_gemm_mx(gp, s)
               : (p->dtype == MOE_DTYPE_BF16 ? launch_grouped_gemm_bf16(gp, s) : launch_grouped_gemm_f32(gp, s));
   if (e != hipSuccess) return MOE_ERR_HIP;

@@ -57,7 +57,8 @@ __device__ __forceinline__ bool split_pays(int nk, int s, bool halfable) {
 template <int LAYER, bool OUT8 = false>
 __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(Bf16GemmArgs args,
                                                                          const int32_t* __restrict__ offsets, int G,
-                                                                         int xcd_slots, SplitWs split) {
+                                                                         int xcd_slots, SplitWs split,
+                                                                         uint32_t shuffle) {
   __shared__ __attribute__((aligned(16))) char lds[kGemmLdsBytes];
   __shared__ TileLds tl;
   const int NT = (args.N + (LAYER == 0 ? kL0Cols : kL1Cols) - 1) / (LAYER == 0 ? kL0Cols : kL1Cols);
@@ -77,13 +78,14 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(Bf16Gem
     if (s >= 2) {
       const int tail0 = T - r;
       const int entries = tail0 + r * s;
+      const Shuffle sm = make_shuffle(shuffle, tail0), st = make_shuffle(shuffle, r);
       for (int v = xcd_slot(blockIdx.x, grid); v < entries; v += grid) {
         if (v < tail0) {
-          const TileCoord c = tile_coord(v, G, NT, kTileRows, xcd_slots, rtb, tl);
+          const TileCoord c = tile_coord(shuffled(sm, v), G, NT, kTileRows, xcd_slots, rtb, tl);
           bf16_gemm_row_tile<LAYER>(args, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], c.m0, c.nt, lds);
         } else {
           const int u = v - tail0, jj = u / s, ck = u - jj * s;
-          const TileCoord c = tile_coord(tail0 + jj, G, NT, kTileRows, xcd_slots, rtb, tl);
+          const TileCoord c = tile_coord(tail0 + shuffled(st, jj), G, NT, kTileRows, xcd_slots, rtb, tl);
           if (ck == 0 && threadIdx.x == 0) {
             int32_t* d = split.desc + 4 * jj;
             d[0] = tl.seg_start[c.g];
@@ -101,13 +103,14 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(Bf16Gem
   }
   const int half = (r > 0 && 2 * r <= grid && T > grid) ? r : 0;  // tiles of the last round to halve
   const int entries = T + half;
+  const Shuffle sm = make_shuffle(shuffle, T - half), sh = make_shuffle(shuffle, half);
   for (int v = xcd_slot(blockIdx.x, grid); v < entries; v += grid) {
     if (v < T - half) {
-      const TileCoord c = tile_coord(v, G, NT, kTileRows, xcd_slots, rtb, tl);
+      const TileCoord c = tile_coord(shuffled(sm, v), G, NT, kTileRows, xcd_slots, rtb, tl);
       bf16_gemm_row_tile<LAYER, false, OUT8>(args, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], c.m0, c.nt, lds);
     } else {
       const int j = v - (T - half);
-      const TileCoord c = tile_coord(T - half + j / 2, G, NT, kTileRows, xcd_slots, rtb, tl);
+      const TileCoord c = tile_coord(T - half + shuffled(sh, j / 2), G, NT, kTileRows, xcd_slots, rtb, tl);
       const int m0 = c.m0 + (j & 1) * (kTileRows / 2);
       if (m0 < tl.seg_rows[c.g])
         bf16_gemm_tile<LAYER, false, kTileRows / 2, false, OUT8>(args, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], m0,
@@ -130,7 +133,8 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_kernel(Bf16Gem
 template <int LAYER>
 __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_expert_kernel(Bf16GemmArgs args,
                                                                                 const int32_t* __restrict__ offsets,
-                                                                                int G, int xcd_slots) {
+                                                                                int G, int xcd_slots,
+                                                                                uint32_t shuffle) {
   __shared__ __attribute__((aligned(16))) char lds[kGemmLdsBytes];
   __shared__ TileLds tl;
   __shared__ int rowpos[kTileRows];
@@ -142,10 +146,12 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_expert_kernel(
   const int r = T % grid;
   const int half = (r > 0 && 2 * r <= grid && T > grid) ? r : 0;  // tiles of the last round to halve
   const int entries = T + half;
+  const Shuffle sm = make_shuffle(shuffle, T - half), sh = make_shuffle(shuffle, half);
   for (int v = xcd_slot(blockIdx.x, grid); v < entries; v += grid) {
     const bool is_half = v >= T - half;
     const int j = v - (T - half);
-    const TileCoord c = tile_coord(is_half ? T - half + j / 2 : v, EL, NT, kTileRows, xcd_slots, rtb, tl);
+    const TileCoord c = tile_coord(is_half ? T - half + shuffled(sh, j / 2) : shuffled(sm, v), EL, NT, kTileRows,
+                                   xcd_slots, rtb, tl);
     const int m0 = is_half ? c.m0 + (j & 1) * (kTileRows / 2) : c.m0;
     const int n = tl.expert_rows[c.g];
     if (m0 >= n) continue;
@@ -165,7 +171,7 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_bf16_expert_kernel(
 // tile; no split of the last round.
 __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_mx_kernel(Bf16GemmArgs args,
                                                                        const int32_t* __restrict__ offsets, int G,
-                                                                       int xcd_slots) {
+                                                                       int xcd_slots, uint32_t shuffle) {
   __shared__ __attribute__((aligned(16))) char lds[kGemmLdsBytes];
   __shared__ TileLds tl;
   const int NT = (args.N + kL1Cols - 1) / kL1Cols;
@@ -175,16 +181,17 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_mx_kernel(Bf16GemmA
   const int r = T % grid;
   const int half = (r > 0 && 2 * r <= grid && T > grid) ? r : 0;
   const int entries = T + half;
+  const Shuffle sm = make_shuffle(shuffle, T - half), sh = make_shuffle(shuffle, half);
   for (int v = xcd_slot(blockIdx.x, grid); v < entries; v += grid) {
     if (v < T - half) {
-      const TileCoord c = tile_coord(v, G, NT, kTileRows, xcd_slots, rtb, tl);
+      const TileCoord c = tile_coord(shuffled(sm, v), G, NT, kTileRows, xcd_slots, rtb, tl);
       if (tl.seg_rows[c.g] <= kTileRows / 2)
         mx_gemm_tile<kTileRows / 2>(args, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], c.m0, c.nt, lds);
       else
         mx_gemm_tile<kTileRows>(args, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], c.m0, c.nt, lds);
     } else {
       const int j = v - (T - half);
-      const TileCoord c = tile_coord(T - half + j / 2, G, NT, kTileRows, xcd_slots, rtb, tl);
+      const TileCoord c = tile_coord(T - half + shuffled(sh, j / 2), G, NT, kTileRows, xcd_slots, rtb, tl);
       const int m0 = c.m0 + (j & 1) * (kTileRows / 2);
       if (m0 < tl.seg_rows[c.g]) mx_gemm_tile<kTileRows / 2>(args, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], m0, c.nt, lds);
     }
@@ -285,7 +292,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(const float* __re
                                                                const float* __restrict__ W0,
                                                                const float* __restrict__ W1, float* __restrict__ C,
                                                                int K, int N, int E, const int32_t* __restrict__ offsets,
-                                                               int G) {
+                                                               int G, uint32_t shuffle) {
   __shared__ float xs[kF32Rows][kF32BK + 1];
   __shared__ float ws[kF32Rows][kF32BK + 1];
   __shared__ TileLds tl;
@@ -293,8 +300,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32_kernel(const float* __re
   const int NT = (N + cols - 1) / cols;
   const int total = build_tile_table(offsets, G, kF32Rows, tl) * NT;
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const Shuffle sm = make_shuffle(shuffle, total);
   for (int v = blockIdx.x; v < total; v += gridDim.x) {
-    const TileCoord c = tile_coord(v, G, NT, kF32Rows, 1, 0, tl);
+    const TileCoord c = tile_coord(shuffled(sm, v), G, NT, kF32Rows, 1, 0, tl);
     const int e = c.g % E, s0 = tl.seg_start[c.g], nrows = tl.seg_rows[c.g];
     const int col0 = c.nt * cols;
     const int64_t ebase = (int64_t)e * N * K;
@@ -393,9 +401,9 @@ hipError_t launch_grouped_gemm_bf16(const GemmProblem& gp, hipStream_t s) {
   if (gp.rowmap) {
     a.M = gp.R;  // rows of the token-row buffer, read at their own positions
     if (gp.layer == 0)
-      grouped_gemm_bf16_expert_kernel<0><<<grid, kGemmThreads, 0, s>>>(a, gp.offsets, gp.G, xcd_slots);
+      grouped_gemm_bf16_expert_kernel<0><<<grid, kGemmThreads, 0, s>>>(a, gp.offsets, gp.G, xcd_slots, gp.shuffle);
     else
-      grouped_gemm_bf16_expert_kernel<1><<<grid, kGemmThreads, 0, s>>>(a, gp.offsets, gp.G, xcd_slots);
+      grouped_gemm_bf16_expert_kernel<1><<<grid, kGemmThreads, 0, s>>>(a, gp.offsets, gp.G, xcd_slots, gp.shuffle);
     return hipGetLastError();
   }
   SplitWs sp{nullptr, nullptr, nullptr};
@@ -407,9 +415,9 @@ hipError_t launch_grouped_gemm_bf16(const GemmProblem& gp, hipStream_t s) {
     sp.part = reinterpret_cast<float*>(w + kSplitHdrBytes);
   }
   if (gp.layer == 0)
-    grouped_gemm_bf16_kernel<0><<<grid, kGemmThreads, 0, s>>>(a, gp.offsets, gp.G, xcd_slots, sp);
+    grouped_gemm_bf16_kernel<0><<<grid, kGemmThreads, 0, s>>>(a, gp.offsets, gp.G, xcd_slots, sp, gp.shuffle);
   else
-    grouped_gemm_bf16_kernel<1><<<grid, kGemmThreads, 0, s>>>(a, gp.offsets, gp.G, xcd_slots, sp);
+    grouped_gemm_bf16_kernel<1><<<grid, kGemmThreads, 0, s>>>(a, gp.offsets, gp.G, xcd_slots, sp, gp.shuffle);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !sp.hdr) return e;
   grouped_gemm_split_reduce<<<grid, 256, 0, s>>>(a, sp);
@@ -438,7 +446,8 @@ hipError_t launch_grouped_gemm_mx(const GemmProblem& gp, hipStream_t s) {
     a.w1 = (const __bf16*)gp.w1;
     a.c = gp.c;
     a.c_scale = reinterpret_cast<uint8_t*>(gp.c) + gp.R * gp.N;
-    grouped_gemm_bf16_kernel<0, true><<<grid, kGemmThreads, 0, s>>>(a, gp.offsets, gp.G, xcd_slots, SplitWs{});
+    grouped_gemm_bf16_kernel<0, true><<<grid, kGemmThreads, 0, s>>>(a, gp.offsets, gp.G, xcd_slots, SplitWs{},
+                                                                     gp.shuffle);
   } else {
     // Hact and W_down MXFP8 (codes, then scales); Y f32
     a.a = (const __bf16*)gp.a;
@@ -449,7 +458,7 @@ hipError_t launch_grouped_gemm_mx(const GemmProblem& gp, hipStream_t s) {
     a.w_scale_bytes = (uint32_t)mx_scale_bytes((int64_t)gp.E * gp.N, gp.K);
     a.w1 = nullptr;
     a.c = gp.c;
-    grouped_gemm_mx_kernel<<<grid, kGemmThreads, 0, s>>>(a, gp.offsets, gp.G, xcd_slots);
+    grouped_gemm_mx_kernel<<<grid, kGemmThreads, 0, s>>>(a, gp.offsets, gp.G, xcd_slots, gp.shuffle);
   }
   return hipGetLastError();
 }
@@ -469,10 +478,10 @@ hipError_t launch_grouped_gemm_f32(const GemmProblem& gp, hipStream_t s) {
   const int grid = device_cu_count() * 2;
   if (gp.layer == 0)
     grouped_gemm_f32_kernel<0><<<grid, 256, 0, s>>>((const float*)gp.a, (const float*)gp.w0, (const float*)gp.w1,
-                                                     (float*)gp.c, gp.K, gp.N, gp.E, gp.offsets, gp.G);
+                                                     (float*)gp.c, gp.K, gp.N, gp.E, gp.offsets, gp.G, gp.shuffle);
   else
     grouped_gemm_f32_kernel<1><<<grid, 256, 0, s>>>((const float*)gp.a, (const float*)gp.w0, nullptr,
-                                                    (float*)gp.c, gp.K, gp.N, gp.E, gp.offsets, gp.G);
+                                                    (float*)gp.c, gp.K, gp.N, gp.E, gp.offsets, gp.G, gp.shuffle);
   return hipGetLastError();
 }
 

@@ -58,6 +58,7 @@ struct GemmProblem {
   void* ws = nullptr;       // bf16: split workspace of gemm_split_ws_bytes(), or null
   size_t ws_bytes = 0;
   int rowmap = 0;           // bf16: each expert's segments of all source blocks as one (G / E of them)
+  uint32_t shuffle = 0;     // nonzero: tiles in a seeded permutation of their order (debug check)
 };
 // Workspace that lets the bf16 grouped GEMM split its last round along K.
 size_t gemm_split_ws_bytes();

@@ -191,13 +191,17 @@ __global__ __launch_bounds__(kGemmThreads) void fused_layer_kernel(FusedArgs a) 
   const int CB = (int)((a.M + kCombineTokens - 1) / kCombineTokens);  // combine items per chunk
   const bool dedicated = a.n_mover > 0;
   auto chunk_width = [&](int c) { return min(kChunkTiles, nt1 - c * kChunkTiles); };
+  // reordering check: items permuted inside their section (Layer0 tiles,
+  // one chunk's Layer1 tiles, one chunk's combine items); waits still
+  // target earlier sections only
+  const Shuffle s_cb = make_shuffle(a.shuffle, CB);
 
   if ((int)blockIdx.x < a.n_mover) {
     // dedicated combiners: chunk by chunk, token blocks in order
     for (;;) {
       const int v = block_claim(mover_q, &lds_word);
       if (v >= nc * CB) return;
-      const int c = v / CB, tb = v - c * CB;
+      const int c = v / CB, tb = shuffled(s_cb, v - c * CB);
       if (!block_wait(chunkdone + c, MT * chunk_width(c), a.status, limit, &lds_word)) return;
       combine_chunk(a, c, (int64_t)tb * kCombineTokens, min(a.M, (int64_t)(tb + 1) * kCombineTokens), comb_rows,
                     comb_w);
@@ -220,6 +224,7 @@ __global__ __launch_bounds__(kGemmThreads) void fused_layer_kernel(FusedArgs a) 
   const int run = xcd_slots;
   const int q = (nq == 1) ? 0 : (int)(blockIdx.x % kXcds);
   int32_t* my_q = xcd_q + q;
+  const Shuffle s_l0 = make_shuffle(a.shuffle, T0);
   Bf16GemmArgs ga;
   ga.E = a.E;
   ga.s2f = a.s2f;
@@ -230,7 +235,7 @@ __global__ __launch_bounds__(kGemmThreads) void fused_layer_kernel(FusedArgs a) 
     const int v = (i / run) * (nq * run) + q * run + (i % run);
     if (v >= total) return;
     if (v < T0) {
-      const TileCoord c = tile_coord(v, a.G, nt0, kTileRows, xcd_slots, (int64_t)kTileRows * a.H * 2, tl);
+      const TileCoord c = tile_coord(shuffled(s_l0, v), a.G, nt0, kTileRows, xcd_slots, (int64_t)kTileRows * a.H * 2, tl);
       ga.w0 = reinterpret_cast<const __bf16*>(a.w_gate);
       ga.w1 = reinterpret_cast<const __bf16*>(a.w_up);
       ga.c = a.hact;
@@ -268,7 +273,8 @@ __global__ __launch_bounds__(kGemmThreads) void fused_layer_kernel(FusedArgs a) 
       }
     }
     if (is_tile) {
-      const TileCoord c = tile_coord(u, a.G, chunk_width(chunk), kTileRows, xcd_slots, (int64_t)kTileRows * a.F * 2, tl);
+      const int ui = shuffled(make_shuffle(a.shuffle, MT * chunk_width(chunk)), u);
+      const TileCoord c = tile_coord(ui, a.G, chunk_width(chunk), kTileRows, xcd_slots, (int64_t)kTileRows * a.F * 2, tl);
       if (!block_wait(l0done + c.mt, nt0, a.status, limit, &lds_word)) return;
       ga.a = reinterpret_cast<const __bf16*>(a.hact);
       ga.w0 = reinterpret_cast<const __bf16*>(a.w_down);
@@ -280,7 +286,8 @@ __global__ __launch_bounds__(kGemmThreads) void fused_layer_kernel(FusedArgs a) 
       block_signal(chunkdone + chunk, 1);
     } else if (comb_chunk >= 0) {
       if (!block_wait(chunkdone + comb_chunk, MT * chunk_width(comb_chunk), a.status, limit, &lds_word)) return;
-      combine_chunk(a, comb_chunk, (int64_t)u * kCombineTokens, min(a.M, (int64_t)(u + 1) * kCombineTokens),
+      const int tb = shuffled(s_cb, u);
+      combine_chunk(a, comb_chunk, (int64_t)tb * kCombineTokens, min(a.M, (int64_t)(tb + 1) * kCombineTokens),
                     comb_rows, comb_w);
     }
   }

@@ -32,6 +32,7 @@ struct FusedArgs {
   int grid;
   int n_mover;
   int spin_limit;
+  uint32_t shuffle;  // nonzero: items in a seeded permutation inside each section (debug check)
 };
 
 size_t fused_ws_bytes(int64_t M, int H, int F, int E, int k, int S);

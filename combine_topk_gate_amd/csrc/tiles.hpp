@@ -192,6 +192,37 @@ __device__ inline TileCoord tile_coord(int v, int G, int NT, int rows, int xcd_s
   return c;
 }
 
+// Seeded reordering of n interchangeable items (the MOE_DEBUG_SHUFFLE
+// check): i -> (a i + b) mod n with a coprime to n, a bijection of [0, n).
+// Seed 0 gives the identity.  Every output element is computed by one item
+// in a fixed order of its own, so a reordering must not change any bit.
+struct Shuffle {
+  uint32_t a, b, n;
+};
+
+__device__ inline Shuffle make_shuffle(uint32_t seed, int n) {
+  Shuffle s{1u, 0u, n > 1 ? (uint32_t)n : 1u};
+  if (seed == 0 || n <= 1) return s;
+  auto gcd = [](uint32_t x, uint32_t y) {
+    while (y) {
+      const uint32_t t = x % y;
+      x = y;
+      y = t;
+    }
+    return x;
+  };
+  uint32_t a = (seed * 2654435761u) % s.n;
+  if (a == 0) a = 1;
+  while (gcd(a, s.n) != 1) a = a + 1 < s.n ? a + 1 : 1;
+  s.a = a;
+  s.b = ((seed ^ (seed >> 16)) * 40503u) % s.n;
+  return s;
+}
+
+__device__ __forceinline__ int shuffled(const Shuffle& s, int i) {
+  return s.a == 1u && s.b == 0u ? i : (int)(((uint64_t)s.a * (uint32_t)i + s.b) % s.n);
+}
+
 // Virtual slot of workgroup `wg` among `n` workgroups: the workgroups of one
 // XCD get a contiguous run of slots.
 __device__ __forceinline__ int xcd_slot(int wg, int n) {

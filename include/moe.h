@@ -52,6 +52,16 @@
  *     (moe_dispatch, moe_layer), offsets do not start at 0, decrease, or
  *     end past R (moe_grouped_gemm), or flat_to_sorted is outside [-1, R)
  *     (moe_combine).  For debugging only: it synchronises and copies.
+ *   - MOE_DEBUG_SHUFFLE=<seed> (a decimal number, 0 or unset: off) makes the
+ *     grouped GEMMs and the fused layer take their tiles in a seeded
+ *     permutation of the usual order: inside the full rounds, and separately
+ *     inside a last round that is split along k or halved; in the fused
+ *     kernel inside each section of its queue (Layer0 tiles, one chunk's
+ *     Layer1 tiles, one chunk's combine items).  Every output element is
+ *     computed by one item in a fixed order of its own, so results must be
+ *     bit-identical to the usual order ([COMET] §4.1.2: rescheduling does
+ *     not change results); a difference is a scheduling bug.  A check, not
+ *     a mode: the permuted order loses the tiles' cache locality.
  *   - Symbols: M tokens, H hidden, F expert width, E experts routing
  *     chooses from, EL experts held by the call (local_experts, = E unless
  *     set), k = topk, S source blocks, G = S*EL segments, R = M*k routed

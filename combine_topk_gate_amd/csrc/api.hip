@@ -403,6 +403,12 @@ moe_status_t moe_layer_ex(const moe_problem_t* p, const void* x, const float* lo
   o.gather = -1;
   if (opts) o = *opts;
 
+  const int cus = device_cu_count();
+  // n_mover < 0 asks the profiled table, which may pick the kernel chain
+  const int movers = o.n_mover >= 0 ? o.n_mover
+                                    : fused_default_movers(M, p->hidden, p->ffn, p->num_experts, p->topk,
+                                                           p->num_src_blocks, held(p), p->dtype, cus);
+  if (movers == kTableUnusable) return MOE_ERR_INVALID_ARGUMENT;
   if (debug_validate() && M > 0) {
     st = validate_logits(p, (const float*)logits, s);
     if (st == MOE_OK && p->num_src_blocks > 1) st = check_range(src_block, M, 0, p->num_src_blocks, s);
@@ -420,11 +426,6 @@ moe_status_t moe_layer_ex(const moe_problem_t* p, const void* x, const float* lo
   }
   e = launch_route(logits, M, p->num_experts, p->topk, idx, w, s);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  const int cus = device_cu_count();
-  // n_mover < 0 asks the profiled table, which may pick the kernel chain
-  const int movers = o.n_mover >= 0 ? o.n_mover
-                                    : fused_default_movers(M, p->hidden, p->ffn, p->num_experts, p->topk,
-                                                           p->num_src_blocks, held(p), p->dtype, cus);
   const bool fused = o.fused != 0 && p->dtype == MOE_DTYPE_BF16 && movers >= 0;
   if (fused) {
     FusedArgs fa;

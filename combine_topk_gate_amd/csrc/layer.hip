@@ -43,6 +43,13 @@
 // Results are bit-identical to the kernel chain: the tiles run the same
 // tile routine on the same values in the same k order, and the combine
 // uses the same per-element routine.
+#include <cstdlib>
+#include <fstream>
+#include <mutex>
+#include <sstream>
+#include <string>
+#include <vector>
+
 #include "common.hpp"
 #include "gemm_bf16.hpp"
 #include "launch.hpp"
@@ -301,6 +308,11 @@ __global__ __launch_bounds__(kGemmThreads) void fused_layer_kernel(FusedArgs a) 
 // listed run the chain too: on one MI355X the chain was faster on every
 // shape measured, from 300 tokens (47 vs 76 us) to the listed layers, so
 // the fused kernel runs where a caller asks for it (opts->n_mover >= 0).
+// COMET paper review §4.2.2: the split is profiled ahead of time, stored as
+// metadata and looked up at run time.  The table below is the one stored in
+// combine_topk_gate_amd/tuning/mi355x.json; MOE_TUNING_TABLE=<path> makes
+// the library use the entries of that JSON file instead (written by
+// tune_split.py --write on the target GPU).
 struct SplitEntry {
   int64_t M;
   int H, F, E, k, S, EL, movers;  // EL: experts held (E when all are)
@@ -310,14 +322,193 @@ static const SplitEntry kSplitTable[] = {
     {8192, 4096, 14336, 8, 2, 1, 8, -1},
     {16384, 4096, 6400, 16, 2, 1, 16, -1},
     {16384, 7168, 4096, 16, 8, 8, 16, -1},
-    {16384, 7168, 4096, 128, 8, 8, 16, -1},  // 16 of 128 experts held: chain 4.84 ms, fused 5.03 ms
+    {16384, 7168, 4096, 128, 8, 8, 16, -1},  // 16 of 128 experts held
 };
+
+namespace {
+
+// A small reader for the table file: {"entries": [{"M": 8192, "H": 4096,
+// "F": 14336, "E": 8, "k": 2, "S": 1, "EL": 8, "n_mover": -1, ...}, ...]}.
+// Every entry needs those eight integer keys; other keys (strings, numbers,
+// true/false/null) are skipped, and so is everything outside "entries".
+struct TableReader {
+  const std::string& t;
+  size_t i = 0;
+  explicit TableReader(const std::string& text) : t(text) {}
+  void ws() {
+    while (i < t.size() && (t[i] == ' ' || t[i] == '\n' || t[i] == '\r' || t[i] == '\t')) ++i;
+  }
+  bool eat(char c) {
+    ws();
+    if (i < t.size() && t[i] == c) {
+      ++i;
+      return true;
+    }
+    return false;
+  }
+  bool string(std::string* out) {
+    if (!eat('"')) return false;
+    std::string s;
+    while (i < t.size() && t[i] != '"') {
+      if (t[i] == '\\') {
+        if (++i >= t.size()) return false;
+      }
+      s += t[i++];
+    }
+    if (i >= t.size()) return false;
+    ++i;
+    if (out) *out = s;
+    return true;
+  }
+  // a JSON number; *integral tells whether it has no fraction or exponent
+  bool number(double* v, bool* integral) {
+    ws();
+    const size_t j = i;
+    if (i < t.size() && t[i] == '-') ++i;
+    bool digits = false, frac = false;
+    while (i < t.size() && ((t[i] >= '0' && t[i] <= '9') || t[i] == '.' || t[i] == 'e' || t[i] == 'E' ||
+                            ((t[i] == '+' || t[i] == '-') && i > j && (t[i - 1] == 'e' || t[i - 1] == 'E')))) {
+      if (t[i] >= '0' && t[i] <= '9') digits = true; else frac = true;
+      ++i;
+    }
+    if (!digits) return false;
+    char* end = nullptr;
+    const std::string s = t.substr(j, i - j);
+    *v = std::strtod(s.c_str(), &end);
+    *integral = !frac;
+    return end && *end == 0;
+  }
+  bool literal() {
+    ws();
+    for (const char* w : {"true", "false", "null"}) {
+      const size_t n = std::char_traits<char>::length(w);
+      if (t.compare(i, n, w) == 0) {
+        i += n;
+        return true;
+      }
+    }
+    return false;
+  }
+  // skips any value (for keys outside "entries")
+  bool skip_value() {
+    ws();
+    if (i >= t.size()) return false;
+    if (t[i] == '"') return string(nullptr);
+    if (t[i] == '{' || t[i] == '[') {
+      const char close = t[i] == '{' ? '}' : ']';
+      const bool obj = t[i] == '{';
+      ++i;
+      if (eat(close)) return true;
+      do {
+        if (obj && (!string(nullptr) || !eat(':'))) return false;
+        if (!skip_value()) return false;
+      } while (eat(','));
+      return eat(close);
+    }
+    if (literal()) return true;
+    double v;
+    bool integral;
+    return number(&v, &integral);
+  }
+  bool entry(SplitEntry* e) {
+    if (!eat('{')) return false;
+    static const char* keys[8] = {"M", "H", "F", "E", "k", "S", "EL", "n_mover"};
+    int64_t val[8];
+    bool seen[8] = {false, false, false, false, false, false, false, false};
+    if (!eat('}')) {
+      do {
+        std::string key;
+        if (!string(&key) || !eat(':')) return false;
+        int which = -1;
+        for (int q = 0; q < 8; ++q)
+          if (key == keys[q]) which = q;
+        if (which < 0) {
+          if (!skip_value()) return false;
+          continue;
+        }
+        double v;
+        bool integral;
+        if (!number(&v, &integral) || !integral || v < -1 || v > 9.0e15) return false;
+        val[which] = (int64_t)v;
+        seen[which] = true;
+      } while (eat(','));
+      if (!eat('}')) return false;
+    }
+    for (int q = 0; q < 8; ++q)
+      if (!seen[q]) return false;
+    for (int q = 1; q < 8; ++q)
+      if (val[q] > 0x7fffffff) return false;
+    *e = SplitEntry{val[0], (int)val[1], (int)val[2], (int)val[3], (int)val[4], (int)val[5], (int)val[6], (int)val[7]};
+    return true;
+  }
+  bool table(std::vector<SplitEntry>* out) {
+    if (!eat('{')) return false;
+    bool found = false;
+    if (!eat('}')) {
+      do {
+        std::string key;
+        if (!string(&key) || !eat(':')) return false;
+        if (key != "entries") {
+          if (!skip_value()) return false;
+          continue;
+        }
+        if (found || !eat('[')) return false;
+        found = true;
+        if (!eat(']')) {
+          do {
+            SplitEntry e;
+            if (!entry(&e)) return false;
+            out->push_back(e);
+          } while (eat(','));
+          if (!eat(']')) return false;
+        }
+      } while (eat(','));
+      if (!eat('}')) return false;
+    }
+    ws();
+    return found && i == t.size();
+  }
+};
+
+std::mutex g_table_mu;
+std::string g_table_path;           // file the entries below came from
+std::vector<SplitEntry> g_table;    // its entries
+bool g_table_ok = false;
+
+// The entries to use: the file MOE_TUNING_TABLE names (read again when the
+// variable changes), else the compiled-in table.  false: the variable is
+// set but the file cannot be read or parsed.
+bool split_table(std::vector<SplitEntry>* out) {
+  const char* path = std::getenv("MOE_TUNING_TABLE");
+  if (!path || !*path) {
+    out->assign(std::begin(kSplitTable), std::end(kSplitTable));
+    return true;
+  }
+  std::lock_guard<std::mutex> lock(g_table_mu);
+  if (g_table_path != path) {
+    g_table_path = path;
+    g_table.clear();
+    std::ifstream f(path, std::ios::binary);
+    std::stringstream buf;
+    if (f) buf << f.rdbuf();
+    const std::string text = buf.str();
+    TableReader r(text);
+    g_table_ok = f.good() || f.eof() ? r.table(&g_table) : false;
+    if (!g_table_ok) g_table.clear();
+  }
+  *out = g_table;
+  return g_table_ok;
+}
+
+}  // namespace
 
 int fused_default_movers(int64_t M, int H, int F, int E, int k, int S, int EL, int dtype, int cus) {
   if (dtype != MOE_DTYPE_BF16) return -1;
-  for (const SplitEntry& s : kSplitTable)
+  std::vector<SplitEntry> table;
+  if (!split_table(&table)) return kTableUnusable;
+  for (const SplitEntry& s : table)
     if (s.M == M && s.H == H && s.F == F && s.E == E && s.k == k && s.S == S && s.EL == EL)
-      return s.movers < cus ? s.movers : 0;
+      return s.movers < 0 ? -1 : (s.movers < cus ? s.movers : 0);
   return -1;
 }
 

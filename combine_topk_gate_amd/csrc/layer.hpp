@@ -37,7 +37,9 @@ struct FusedArgs {
 
 size_t fused_ws_bytes(int64_t M, int H, int F, int E, int k, int S);
 int fused_mt_max(int64_t M, int H, int k, int G);
-// EL: experts held (E when all are).
+// EL: experts held (E when all are).  kTableUnusable: MOE_TUNING_TABLE names
+// a file that cannot be read or parsed.
+constexpr int kTableUnusable = -2;
 int fused_default_movers(int64_t M, int H, int F, int E, int k, int S, int EL, int dtype, int cus);
 moe_status_t fused_check(const FusedArgs& a, int cus);
 hipError_t launch_fused_layer(const FusedArgs& a, hipStream_t s);

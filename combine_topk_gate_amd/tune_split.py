@@ -6,9 +6,11 @@ For each workload it times moe_layer as the kernel chain and as the fused
 kernel with every candidate number of dedicated combine workgroups
 (0 = combine items in the shared queue), and prints one JSON line per
 workload plus the C++ table rows (the split table in csrc/layer.hip) for the
-fastest fused split.  The split is picked ahead of time and looked up at
-run time, as COMET does with its profiled per-shape metadata (paper review
-§4.2.2).
+fastest fused split; with --write PATH it also writes them as the JSON table
+the library reads when MOE_TUNING_TABLE=PATH is set (the format of
+combine_topk_gate_amd/tuning/mi355x.json).  The split is picked ahead of
+time and looked up at run time, as COMET does with its profiled per-shape
+metadata (paper review §4.2.2).
 """
 from __future__ import annotations
 
@@ -30,6 +32,7 @@ def main():
     ap.add_argument("--movers", default="0,2,4,8,16,32")
     ap.add_argument("--reps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--write", default="", help="write the table as JSON to this path")
     args = ap.parse_args()
 
     import torch
@@ -44,7 +47,7 @@ def main():
             return torch.from_numpy(a.view(np.int16)).to("cuda:0").view(torch.bfloat16)
         return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
 
-    rows = []
+    rows, entries = [], []
     for name in args.configs.split(","):
         cfg = moe_synth.config(name)
         d = moe_synth.make_inputs(cfg)
@@ -81,9 +84,23 @@ def main():
         # the chain where it beats every fused split
         m = -1 if res["chain_us"] < best[0] else m
         rows.append(f"    {{{cfg.M}, {cfg.H}, {cfg.F}, {cfg.E}, {cfg.k}, {cfg.S}, {cfg.EL}, {m}}},")
+        entries.append({"config": name, "M": cfg.M, "H": cfg.H, "F": cfg.F, "E": cfg.E, "k": cfg.k, "S": cfg.S,
+                        "EL": cfg.EL, "n_mover": m, "chain_us": round(res["chain_us"]),
+                        "best_fused_us": round(best[0])})
         del g, ws, out
         torch.cuda.empty_cache()
     print("\n".join(rows))
+    if args.write:
+        props = torch.cuda.get_device_properties(0)
+        table = {"device": f"{props.name} ({props.multi_processor_count} CUs, one workgroup per CU)",
+                 "written_by": "python -m combine_topk_gate_amd.tune_split --write " + args.write,
+                 "meaning": "n_mover: dedicated combine workgroups of the fused layer (0: combine items in the "
+                            "shared queue); -1: the kernel chain, faster than every fused split. Shapes not "
+                            "listed run the chain.",
+                 "entries": entries}
+        with open(args.write, "w") as fh:
+            json.dump(table, fh, indent=2)
+            fh.write("\n")
 
 
 if __name__ == "__main__":

@@ -52,6 +52,17 @@
  *     (moe_dispatch, moe_layer), offsets do not start at 0, decrease, or
  *     end past R (moe_grouped_gemm), or flat_to_sorted is outside [-1, R)
  *     (moe_combine).  For debugging only: it synchronises and copies.
+ *   - MOE_TUNING_TABLE=<path> makes moe_layer's plan (the split table of
+ *     the fused layer, used when opts->n_mover < 0) come from that JSON file
+ *     instead of the table compiled in (the one stored in
+ *     combine_topk_gate_amd/tuning/mi355x.json): {"entries": [{"M": .., "H":
+ *     .., "F": .., "E": .., "k": .., "S": .., "EL": .., "n_mover": ..}, ...]}
+ *     with n_mover -1 for the kernel chain; other keys are ignored.
+ *     combine_topk_gate_amd/tune_split.py --write profiles a GPU and writes
+ *     one.  A file that cannot be read or parsed makes moe_layer return
+ *     MOE_ERR_INVALID_ARGUMENT (when it needs the plan) and
+ *     moe_layer_default_movers return -2; it is read again when the
+ *     variable changes.
  *   - MOE_DEBUG_SHUFFLE=<seed> (a decimal number, 0 or unset: off) makes the
  *     grouped GEMMs and the fused layer take their tiles in a seeded
  *     permutation of the usual order: inside the full rounds, and separately
@@ -353,7 +364,8 @@ moe_status_t moe_layer_ex(const moe_problem_t* p, const void* x, const float* lo
  * layer runs as the kernel chain (f32 and MXFP8 layers, shapes where
  * profiling found the chain faster, and shapes the table does not list:
  * on MI355X the chain was faster on every shape measured) or the problem
- * is invalid. */
+ * is invalid; -2 when MOE_TUNING_TABLE names a file that cannot be read or
+ * parsed. */
 int32_t moe_layer_default_movers(const moe_problem_t* p);
 
 /* Synchronises `stream` and returns the device status the last moe_layer

@@ -6,6 +6,8 @@ the same order as in the kernel chain, whatever the split between mover and
 matrix-core workgroups or the grid size; so any bitwise difference from the
 chain is a race or a flag bug.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -134,3 +136,26 @@ def test_invalid_split_is_rejected(qwen):
     with pytest.raises(moe.MoeError) as ei:
         run_layer(cfg, g, n_mover=4, grid=1 << 20)
     assert ei.value.status == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_unusable_tuning_table_is_an_error(qwen, tmp_path):
+    # the plan comes from MOE_TUNING_TABLE when set: a file that cannot be
+    # parsed fails the call before anything is launched; an explicit split
+    # needs no plan
+    cfg, g, chain = qwen
+    bad = tmp_path / "bad.json"
+    bad.write_text('{"entries": [{"M": 1}]}')
+    old = os.environ.get("MOE_TUNING_TABLE")
+    os.environ["MOE_TUNING_TABLE"] = str(bad)
+    try:
+        with pytest.raises(moe.MoeError) as ei:
+            run_layer(cfg, g)
+        assert ei.value.status == moe.MOE_ERR_INVALID_ARGUMENT
+        out, _, status = run_layer(cfg, g, n_mover=0)
+        assert status == moe.MOE_OK
+        assert torch.equal(out, chain["out"])
+    finally:
+        if old is None:
+            del os.environ["MOE_TUNING_TABLE"]
+        else:
+            os.environ["MOE_TUNING_TABLE"] = old

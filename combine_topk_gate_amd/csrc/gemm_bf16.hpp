@@ -65,7 +65,7 @@ struct Bf16GemmArgs {
   uint32_t a_scale_bytes, w_scale_bytes;
   int K, N, E;
   // gather mode (layer 0 inside the fused layer): sorted row r reads token
-  // row sorted_to_flat[r] / topk of x directly, so X_perm is never written
+  // row sorted_to_flat[r] / topk of x directly, so X_perm need not be written
   const int32_t* s2f;
   int topk;
   int64_t M;

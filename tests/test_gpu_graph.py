@@ -62,3 +62,67 @@ def test_layer_graph_replays_equal_eager(dtype, fused):
         assert moe.moe_debug_device_status(p, ws) == moe.MOE_OK
         assert torch.equal(out_g, out_e), rep
     assert not torch.equal(inputs[0][0], inputs[1][0])
+
+
+@pytest.mark.parametrize("name,cfg", [
+    ("summed", moe_synth.Config("gdisp", 2048, 4096, 256, 8, 2, 1, "bf16", 43)),
+    # 32 chunks x 1024 segments: past what one workgroup sums, so the
+    # histograms are scanned by a third launch first
+    ("scanned", moe_synth.Config("gdisp_s", 8192, 256, 256, 128, 8, 8, "bf16", 44, 0.0, 1024)),
+])
+def test_dispatch_noalloc_graph_replays_equal_eager(name, cfg):
+    """The allocation-free dispatch is for callers that cannot allocate, such
+    as code under graph capture: captured once, each replay must give what the
+    allocating moe_dispatch gives eagerly on the same (changed) inputs."""
+    print(f"[graph] dispatch_noalloc {name} {cfg}", flush=True)
+    g = upload(moe_synth.make_inputs(cfg))
+    p = problem_of(cfg)
+    M, k, H, G, R = cfg.M, cfg.k, cfg.H, cfg.S * cfg.EL, cfg.M * cfg.k
+    idx = torch.empty((M, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((M, k), dtype=torch.float32, device="cuda")
+
+    def bufs():
+        return dict(counts=torch.empty(G, dtype=torch.int32, device="cuda"),
+                    offsets=torch.empty(G + 1, dtype=torch.int32, device="cuda"),
+                    s2f=torch.empty(R, dtype=torch.int32, device="cuda"),
+                    f2s=torch.empty(R, dtype=torch.int32, device="cuda"),
+                    xp=torch.empty((R, H), dtype=torch.bfloat16, device="cuda"))
+
+    e, gr = bufs(), bufs()
+    ws = torch.empty(max(moe.moe_workspace_bytes(p, moe.MOE_OP_DISPATCH), 4), dtype=torch.uint8, device="cuda")
+    src = g.get("src_block")
+
+    def noalloc():
+        moe.moe_dispatch_noalloc(p, g["x"], idx, src, gr["counts"], gr["offsets"], gr["s2f"], gr["f2s"], gr["xp"])
+
+    moe.moe_route(p, g["logits"], idx, w)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        noalloc()  # warm-up outside the capture (the scratch address is looked up once)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        noalloc()
+    torch.cuda.synchronize()
+    inputs = [(g["x"].clone(), g["logits"].clone()),
+              ((g["x"].float() * -0.5).to(torch.bfloat16), g["logits"].flip(1).contiguous()),
+              (g["x"].clone(), g["logits"].clone())]
+    for rep, (xv, lv) in enumerate(inputs):
+        g["x"].copy_(xv)
+        g["logits"].copy_(lv)
+        moe.moe_route(p, g["logits"], idx, w)
+        moe.moe_dispatch(p, g["x"], idx, src, e["counts"], e["offsets"], e["s2f"], e["f2s"], e["xp"], ws)
+        torch.cuda.synchronize()
+        for key in ("counts", "offsets", "s2f", "f2s"):
+            gr[key].fill_(-7)
+        gr["xp"].fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for key in ("counts", "offsets", "s2f", "f2s"):
+            assert torch.equal(gr[key], e[key]), (name, rep, key)
+        n = int(e["offsets"][-1])
+        assert n == R, (name, n)  # every expert is held: every pair kept
+        assert torch.equal(gr["xp"][:n].view(torch.int16), e["xp"][:n].view(torch.int16)), (name, rep)
+    assert not torch.equal(inputs[0][1], inputs[1][1])

@@ -39,7 +39,8 @@ MOE_OP_LAYER = 2
 MOE_NOALLOC_SCRATCH_BYTES = 1 << 20
 
 EXPORTED = ("moe_workspace_bytes", "moe_route", "moe_dispatch", "moe_dispatch_noalloc", "moe_grouped_gemm", "moe_combine", "moe_combine_ex",
-            "moe_layer", "moe_layer_ex", "moe_quantize_mxfp8", "moe_layer_default_movers", "moe_debug_device_status",
+            "moe_layer", "moe_layer_ex", "moe_quantize_mxfp8", "moe_transpose_weights", "moe_layer_default_movers",
+            "moe_debug_device_status",
             "moe_status_string", "moe_abi_version")
 
 
@@ -95,6 +96,7 @@ def load_library(path: str = LIB_PATH):
         "moe_layer_ex": ([PP, P, P, P, P, P, P, ctypes.POINTER(Epilogue), P, ctypes.POINTER(LayerAux),
                           ctypes.POINTER(LayerOpts), P, SZ, P], I32),
         "moe_quantize_mxfp8": ([ctypes.c_int64, I32, I32, P, P, P], I32),
+        "moe_transpose_weights": ([ctypes.c_int64, I32, I32, I32, P, P, P], I32),
         "moe_layer_default_movers": ([PP], I32),
         "moe_debug_device_status": ([PP, P, SZ, P], I32),
         "moe_status_string": ([I32], ctypes.c_char_p),
@@ -219,6 +221,17 @@ def moe_quantize_mxfp8(src, dst, stream=None):
     dt = MOE_DTYPE_BF16 if src.dtype == torch.bfloat16 else MOE_DTYPE_F32
     _check(load_library().moe_quantize_mxfp8(rows, cols, dt, _ptr(src), _ptr(dst), _stream(stream)),
            "moe_quantize_mxfp8")
+
+
+def moe_transpose_weights(src, dst, stream=None):
+    """dst[b] = src[b].T for a [batch, rows, cols] bf16/f32 tensor src and a
+    [batch, cols, rows] tensor dst of the same dtype (weights given as the
+    math writes them -> the storage the layer reads)."""
+    import torch
+    batch, rows, cols = (1,) * (3 - src.dim()) + tuple(src.shape)
+    dt = MOE_DTYPE_BF16 if src.dtype == torch.bfloat16 else MOE_DTYPE_F32
+    _check(load_library().moe_transpose_weights(batch, rows, cols, dt, _ptr(src), _ptr(dst), _stream(stream)),
+           "moe_transpose_weights")
 
 
 def moe_layer(p, x, logits, src_block, w_gate, w_up, w_down, out, ws, aux: dict | None = None,

@@ -518,6 +518,19 @@ moe_status_t moe_quantize_mxfp8(int64_t rows, int32_t cols, int32_t src_dtype, c
   return hip_status(launch_mx_quantize(src, src_dtype == MOE_DTYPE_BF16, rows, cols, dst, (hipStream_t)stream));
 }
 
+moe_status_t moe_transpose_weights(int64_t batch, int32_t rows, int32_t cols, int32_t dtype, const void* src,
+                                   void* dst, void* stream) {
+  if (batch < 0 || rows <= 0 || cols <= 0 || rows % 64 || cols % 64) return MOE_ERR_INVALID_ARGUMENT;
+  if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_F32) return MOE_ERR_INVALID_ARGUMENT;
+  if (batch == 0) return MOE_OK;
+  if (!src || !dst || !aligned(src, 16) || !aligned(dst, 16)) return MOE_ERR_INVALID_ARGUMENT;
+  const uint64_t bytes = (uint64_t)batch * (uint64_t)rows * (uint64_t)cols * (dtype == MOE_DTYPE_BF16 ? 2u : 4u);
+  if ((uint64_t)batch * rows * (uint64_t)cols >= (1ull << 40)) return MOE_ERR_UNSUPPORTED;
+  const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst;
+  if (a < b + bytes && b < a + bytes) return MOE_ERR_INVALID_ARGUMENT;  // overlapping buffers
+  return hip_status(launch_transpose(src, dst, batch, rows, cols, dtype == MOE_DTYPE_BF16, (hipStream_t)stream));
+}
+
 moe_status_t moe_debug_device_status(const moe_problem_t* p, void* ws, size_t ws_bytes, void* stream) {
   moe_status_t st = check_problem(p);
   if (st != MOE_OK) return st;

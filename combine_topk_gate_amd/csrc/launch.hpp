@@ -71,6 +71,9 @@ hipError_t launch_grouped_gemm_f32(const GemmProblem& gp, hipStream_t s);
 // (r / 32) * cols + (b / 4) * 128 + (r % 32) * 4 + b % 4.
 hipError_t launch_grouped_gemm_mx(const GemmProblem& gp, hipStream_t s);
 hipError_t launch_mx_quantize(const void* src, int src_bf16, int64_t rows, int cols, void* dst, hipStream_t s);
+// Batched transpose src [batch, rows, cols] -> dst [batch, cols, rows]; rows
+// and cols multiples of 64; bf16 (else f32) elements.
+hipError_t launch_transpose(const void* src, void* dst, int64_t batch, int rows, int cols, bool bf16, hipStream_t s);
 
 hipError_t launch_combine(const float* y, const float* topk_w, const int32_t* flat_to_sorted, int64_t M, int H,
                           int k, const OutEpilogue& ep, hipStream_t s);

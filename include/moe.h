@@ -350,6 +350,21 @@ moe_status_t moe_layer(const moe_problem_t* p, const void* x, const float* logit
 moe_status_t moe_quantize_mxfp8(int64_t rows, int32_t cols, int32_t src_dtype, const void* src, void* dst,
                                 void* stream);
 
+/*
+ * Weight preparation for callers holding the weight matrices as the math
+ * writes them (reading of the pages' layer: x·W_gate with W_gate of H x F,
+ * h·W_down with W_down of F x H): a batched transpose src [batch, rows,
+ * cols] -> dst [batch, cols, rows] that gives the storage the layer reads
+ * (W_gate, W_up: batch = EL, rows = H, cols = F -> [EL,F,H]; W_down: rows =
+ * F, cols = H -> [EL,H,F]).  dtype MOE_DTYPE_BF16 or MOE_DTYPE_F32 (for an
+ * MXFP8 layer, transpose the bf16 W_down, then moe_quantize_mxfp8 it).
+ * rows and cols multiples of 64, src and dst 16-byte aligned and not
+ * overlapping (else MOE_ERR_INVALID_ARGUMENT).  Enqueued on stream; meant
+ * to run once, before the layer calls, not on the hot path.
+ */
+moe_status_t moe_transpose_weights(int64_t batch, int32_t rows, int32_t cols, int32_t dtype, const void* src,
+                                   void* dst, void* stream);
+
 /* moe_layer with the combine's epilogue (NULL epi: as moe_layer); out [M,H]
  * in epi->out_dtype.  The fused kernel and the chain apply it in the same
  * f32 order, so they still agree bit for bit. */

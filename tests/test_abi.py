@@ -198,3 +198,21 @@ def test_noalloc_dispatch_checks_arguments_and_size_on_the_host(lib):
                                (16384, 4096, 6400, 16, 2, 1)]:
         q = moe.problem(M, H, F, E, k, S)
         assert lib.moe_workspace_bytes(ctypes.byref(q), moe.MOE_OP_DISPATCH) <= moe.MOE_NOALLOC_SCRATCH_BYTES
+
+
+def test_weight_transpose_rejects_bad_arguments(lib):
+    # host checks only: nothing here reaches a launch
+    P = ctypes.c_void_p
+    bf16, f32 = moe.MOE_DTYPE_BF16, moe.MOE_DTYPE_F32
+    a, b = P(1 << 32), P((1 << 32) + (1 << 30))
+    INV = moe.MOE_ERR_INVALID_ARGUMENT
+    assert lib.moe_transpose_weights(2, 96, 128, bf16, a, b, None) == INV  # rows not a multiple of 64
+    assert lib.moe_transpose_weights(2, 128, 100, bf16, a, b, None) == INV  # cols not a multiple of 64
+    assert lib.moe_transpose_weights(2, 128, 128, 7, a, b, None) == INV  # dtype
+    assert lib.moe_transpose_weights(-1, 128, 128, bf16, a, b, None) == INV
+    assert lib.moe_transpose_weights(2, 128, 128, bf16, None, b, None) == INV
+    assert lib.moe_transpose_weights(2, 128, 128, bf16, P((1 << 32) + 8), b, None) == INV  # misaligned
+    # overlapping source and destination (2 x 128 x 128 f32 = 128 KiB)
+    assert lib.moe_transpose_weights(2, 128, 128, f32, a, P((1 << 32) + (64 << 10)), None) == INV
+    assert lib.moe_transpose_weights(2, 128, 128, f32, P((1 << 32) + (64 << 10)), a, None) == INV
+    assert lib.moe_transpose_weights(0, 128, 128, bf16, a, b, None) == moe.MOE_OK  # nothing to do

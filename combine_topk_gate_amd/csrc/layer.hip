@@ -475,15 +475,19 @@ std::string g_table_path;           // file the entries below came from
 std::vector<SplitEntry> g_table;    // its entries
 bool g_table_ok = false;
 
-// The entries to use: the file MOE_TUNING_TABLE names (read again when the
-// variable changes), else the compiled-in table.  false: the variable is
-// set but the file cannot be read or parsed.
-bool split_table(std::vector<SplitEntry>* out) {
+// The plan of a shape from the entries in use: the file MOE_TUNING_TABLE
+// names (read when the variable first takes that value), else the
+// compiled-in table.  kTableUnusable: the variable is set but the file
+// cannot be read or parsed.  No allocation once the file has been read.
+int table_lookup(int64_t M, int H, int F, int E, int k, int S, int EL, int cus) {
+  auto find = [&](const SplitEntry* b, const SplitEntry* e) {
+    for (const SplitEntry* s = b; s != e; ++s)
+      if (s->M == M && s->H == H && s->F == F && s->E == E && s->k == k && s->S == S && s->EL == EL)
+        return s->movers < 0 ? -1 : (s->movers < cus ? s->movers : 0);
+    return -1;
+  };
   const char* path = std::getenv("MOE_TUNING_TABLE");
-  if (!path || !*path) {
-    out->assign(std::begin(kSplitTable), std::end(kSplitTable));
-    return true;
-  }
+  if (!path || !*path) return find(std::begin(kSplitTable), std::end(kSplitTable));
   std::lock_guard<std::mutex> lock(g_table_mu);
   if (g_table_path != path) {
     g_table_path = path;
@@ -496,20 +500,15 @@ bool split_table(std::vector<SplitEntry>* out) {
     g_table_ok = f.good() || f.eof() ? r.table(&g_table) : false;
     if (!g_table_ok) g_table.clear();
   }
-  *out = g_table;
-  return g_table_ok;
+  if (!g_table_ok) return kTableUnusable;
+  return find(g_table.data(), g_table.data() + g_table.size());
 }
 
 }  // namespace
 
 int fused_default_movers(int64_t M, int H, int F, int E, int k, int S, int EL, int dtype, int cus) {
   if (dtype != MOE_DTYPE_BF16) return -1;
-  std::vector<SplitEntry> table;
-  if (!split_table(&table)) return kTableUnusable;
-  for (const SplitEntry& s : table)
-    if (s.M == M && s.H == H && s.F == F && s.E == E && s.k == k && s.S == S && s.EL == EL)
-      return s.movers < 0 ? -1 : (s.movers < cus ? s.movers : 0);
-  return -1;
+  return table_lookup(M, H, F, E, k, S, EL, cus);
 }
 
 int fused_mt_max(int64_t M, int H, int k, int G) { return fused_geom(M, H, k, G).mt_max; }

@@ -268,13 +268,25 @@ __global__ __launch_bounds__(256) void grouped_gemm_split_reduce(Bf16GemmArgs ar
     const float* base = split.part + (size_t)jj * s * kSplitPartFloats;
     const int c = threadIdx.x & 63;
     const int n = nt * kL1Cols + 4 * c;
-    for (int t = t0 + (threadIdx.x >> 6); t < t0 + kReduceRows; t += 4) {
-      const int trow = m0 + t;
-      if (trow >= seg_rows || n >= N) continue;
-      f32x4_t ys = {0.f, 0.f, 0.f, 0.f};
-      for (int k = 0; k < s; ++k)
-        ys += *reinterpret_cast<const f32x4_t*>(base + (size_t)k * kSplitPartFloats + (size_t)t * 256 + 4 * c);
-      *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(args.c) + (int64_t)(seg_start + trow) * N + n) = ys;
+    // the thread's 4 rows t0 + (tid / 64) + 4 i accumulate together, so 4
+    // loads are in flight per range; each sum still runs over the ranges in
+    // increasing order from zero (rows past the segment are read from the
+    // partial buffer, which has all 256, and not stored)
+    constexpr int RT = kReduceRows / 4;
+    const int tq = t0 + (threadIdx.x >> 6);
+    f32x4_t ys[RT];
+#pragma unroll
+    for (int i = 0; i < RT; ++i) ys[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < s; ++k) {
+      const float* pk = base + (size_t)k * kSplitPartFloats + 4 * c;
+#pragma unroll
+      for (int i = 0; i < RT; ++i) ys[i] += *reinterpret_cast<const f32x4_t*>(pk + (size_t)(tq + 4 * i) * 256);
+    }
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+      const int trow = m0 + tq + 4 * i;
+      if (trow < seg_rows && n < N)
+        *reinterpret_cast<f32x4_t*>(reinterpret_cast<float*>(args.c) + (int64_t)(seg_start + trow) * N + n) = ys[i];
     }
   }
 }
@@ -420,7 +432,9 @@ hipError_t launch_grouped_gemm_bf16(const GemmProblem& gp, hipStream_t s) {
     grouped_gemm_bf16_kernel<1><<<grid, kGemmThreads, 0, s>>>(a, gp.offsets, gp.G, xcd_slots, sp, gp.shuffle);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !sp.hdr) return e;
-  grouped_gemm_split_reduce<<<grid, 256, 0, s>>>(a, sp);
+  // up to 4 blocks per split tile's 16 items of 16 rows (r <= grid tiles);
+  // blocks past the items exit at once
+  grouped_gemm_split_reduce<<<4 * grid, 256, 0, s>>>(a, sp);
   return hipGetLastError();
 }
 

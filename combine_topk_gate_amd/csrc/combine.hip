@@ -31,30 +31,42 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* _
       w[threadIdx.x] = topk_w[t * k + threadIdx.x];
     }
     __syncthreads();
-    // kCombineUnroll column groups per thread at a time: each slot's loads
-    // for all of them are issued before any is used (the per-element
-    // arithmetic is combine_group's: from zero, slots in order, fmaf)
+    // kCombineUnroll column groups per thread at a time, two slots per
+    // step: both slots' loads for all of them are issued before any is used
+    // (the per-element arithmetic is combine_group's: from zero, slots in
+    // order, fmaf)
     for (int q0 = threadIdx.x; q0 < groups; q0 += kCombineThreads * kCombineUnroll) {
       float4 acc[kCombineUnroll];
 #pragma unroll
       for (int u = 0; u < kCombineUnroll; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int j = 0; j < k; ++j) {
-        const int32_t row = rows[j];
-        if ((uint64_t)(int64_t)row >= (uint64_t)(M * k)) continue;  // -1: a pair of an expert not held here
-        const float wj = w[j];
-        const float* yr = y + (int64_t)row * H;
-        float4 v[kCombineUnroll];
+      for (int j0 = 0; j0 < k; j0 += 2) {
+        float4 v[2][kCombineUnroll];
+        bool held[2];
+        float wj[2];
 #pragma unroll
-        for (int u = 0; u < kCombineUnroll; ++u) {
-          const int q = q0 + u * kCombineThreads;
-          v[u] = q < groups ? *reinterpret_cast<const float4*>(yr + (int64_t)q * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int h = 0; h < 2; ++h) {
+          const int j = j0 + h;
+          const int32_t row = j < k ? rows[j] : -1;
+          held[h] = (uint64_t)(int64_t)row < (uint64_t)(M * k);  // -1: a pair of an expert not held here
+          wj[h] = held[h] ? w[j] : 0.f;
+          const float* yr = y + (int64_t)(held[h] ? row : 0) * H;
+#pragma unroll
+          for (int u = 0; u < kCombineUnroll; ++u) {
+            const int q = q0 + u * kCombineThreads;
+            v[h][u] = held[h] && q < groups ? *reinterpret_cast<const float4*>(yr + (int64_t)q * 4)
+                                            : make_float4(0.f, 0.f, 0.f, 0.f);
+          }
         }
 #pragma unroll
-        for (int u = 0; u < kCombineUnroll; ++u) {
-          acc[u].x = fmaf(wj, v[u].x, acc[u].x);
-          acc[u].y = fmaf(wj, v[u].y, acc[u].y);
-          acc[u].z = fmaf(wj, v[u].z, acc[u].z);
-          acc[u].w = fmaf(wj, v[u].w, acc[u].w);
+        for (int h = 0; h < 2; ++h) {
+          if (!held[h]) continue;
+#pragma unroll
+          for (int u = 0; u < kCombineUnroll; ++u) {
+            acc[u].x = fmaf(wj[h], v[h][u].x, acc[u].x);
+            acc[u].y = fmaf(wj[h], v[h][u].y, acc[u].y);
+            acc[u].z = fmaf(wj[h], v[h][u].z, acc[u].z);
+            acc[u].w = fmaf(wj[h], v[h][u].w, acc[u].w);
+          }
         }
       }
 #pragma unroll

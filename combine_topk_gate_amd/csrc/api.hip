@@ -524,8 +524,10 @@ moe_status_t moe_transpose_weights(int64_t batch, int32_t rows, int32_t cols, in
   if (dtype != MOE_DTYPE_BF16 && dtype != MOE_DTYPE_F32) return MOE_ERR_INVALID_ARGUMENT;
   if (batch == 0) return MOE_OK;
   if (!src || !dst || !aligned(src, 16) || !aligned(dst, 16)) return MOE_ERR_INVALID_ARGUMENT;
-  const uint64_t bytes = (uint64_t)batch * (uint64_t)rows * (uint64_t)cols * (dtype == MOE_DTYPE_BF16 ? 2u : 4u);
-  if ((uint64_t)batch * rows * (uint64_t)cols >= (1ull << 40)) return MOE_ERR_UNSUPPORTED;
+  // sizes bounded before any product that could wrap: batch * rows * cols < 2^40
+  const uint64_t elems = (uint64_t)rows * (uint64_t)cols;  // < 2^62
+  if (elems >= (1ull << 40) || (uint64_t)batch >= (1ull << 40) / elems) return MOE_ERR_UNSUPPORTED;
+  const uint64_t bytes = (uint64_t)batch * elems * (dtype == MOE_DTYPE_BF16 ? 2u : 4u);
   const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst;
   if (a < b + bytes && b < a + bytes) return MOE_ERR_INVALID_ARGUMENT;  // overlapping buffers
   return hip_status(launch_transpose(src, dst, batch, rows, cols, dtype == MOE_DTYPE_BF16, (hipStream_t)stream));

@@ -216,3 +216,8 @@ def test_weight_transpose_rejects_bad_arguments(lib):
     assert lib.moe_transpose_weights(2, 128, 128, f32, a, P((1 << 32) + (64 << 10)), None) == INV
     assert lib.moe_transpose_weights(2, 128, 128, f32, P((1 << 32) + (64 << 10)), a, None) == INV
     assert lib.moe_transpose_weights(0, 128, 128, bf16, a, b, None) == moe.MOE_OK  # nothing to do
+    # sizes past 2^40 elements, including ones whose products would wrap
+    UNS = moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_transpose_weights(1 << 40, 64, 64, bf16, a, b, None) == UNS
+    assert lib.moe_transpose_weights((1 << 62) + 1, 1 << 30, 1 << 30, bf16, a, b, None) == UNS
+    assert lib.moe_transpose_weights(1 << 20, 1 << 14, 1 << 14, f32, a, b, None) == UNS

@@ -62,6 +62,7 @@ moe_status_t check_problem(const moe_problem_t* p) {
   if (p->dtype != MOE_DTYPE_F32 && p->dtype != MOE_DTYPE_BF16 && p->dtype != MOE_DTYPE_BF16_MXFP8)
     return MOE_ERR_INVALID_ARGUMENT;
   if (p->dtype == MOE_DTYPE_BF16_MXFP8 && p->ffn % 128) return MOE_ERR_UNSUPPORTED;
+  if (M >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;  // bounded before M * topk is formed
   const int64_t R = M * p->topk;
   if (R >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
   const int64_t wide = p->hidden > p->ffn ? p->hidden : p->ffn;
@@ -514,7 +515,7 @@ moe_status_t moe_quantize_mxfp8(int64_t rows, int32_t cols, int32_t src_dtype, c
   if (src_dtype != MOE_DTYPE_BF16 && src_dtype != MOE_DTYPE_F32) return MOE_ERR_INVALID_ARGUMENT;
   if (rows == 0) return MOE_OK;
   if (!src || !dst || !aligned(src, 16) || !aligned(dst, 16)) return MOE_ERR_INVALID_ARGUMENT;
-  if (rows * (int64_t)cols >= (1ll << 40)) return MOE_ERR_UNSUPPORTED;
+  if (rows >= (1ll << 40) / cols) return MOE_ERR_UNSUPPORTED;  // rows * cols < 2^40, checked without forming it
   return hip_status(launch_mx_quantize(src, src_dtype == MOE_DTYPE_BF16, rows, cols, dst, (hipStream_t)stream));
 }
 

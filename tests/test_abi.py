@@ -138,6 +138,9 @@ def test_unsupported_sizes(lib):
     # 32-bit element offsets: R * H must stay below 2^31
     p = moe.problem(1 << 20, 4096, 64, 8, 2)
     assert lib.moe_route(ctypes.byref(p), None, None, None, None) == moe.MOE_ERR_UNSUPPORTED
+    # a token count whose product with topk would wrap
+    p = moe.problem((1 << 62) + 3, 4096, 64, 8, 2)
+    assert lib.moe_route(ctypes.byref(p), None, None, None, None) == moe.MOE_ERR_UNSUPPORTED
 
 
 def test_workspace_sizes_cover_intermediates(lib):
@@ -167,6 +170,9 @@ def test_mxfp8_quantiser_rejects_bad_arguments(lib):
     assert lib.moe_quantize_mxfp8(4, 128, moe.MOE_DTYPE_BF16, None, fake, None) == inval
     assert lib.moe_quantize_mxfp8(4, 128, moe.MOE_DTYPE_F32, fake, ctypes.c_void_p((1 << 20) + 8), None) == inval
     assert lib.moe_quantize_mxfp8(0, 128, moe.MOE_DTYPE_BF16, None, None, None) == moe.MOE_OK  # nothing to do
+    # a row count whose product with cols would wrap
+    assert lib.moe_quantize_mxfp8((1 << 62) + 5, 1 << 20, moe.MOE_DTYPE_BF16, fake, fake, None) == \
+        moe.MOE_ERR_UNSUPPORTED
 
 
 def test_mx_buffer_size_matches_the_layout():

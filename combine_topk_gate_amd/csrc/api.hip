@@ -67,7 +67,9 @@ moe_status_t check_problem(const moe_problem_t* p) {
   if (R >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
   const int64_t wide = p->hidden > p->ffn ? p->hidden : p->ffn;
   if (R * wide >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
-  if ((int64_t)held(p) * p->hidden * p->ffn >= (1ll << 31)) return MOE_ERR_UNSUPPORTED;
+  // weights are addressed per expert with 64-bit offsets; the MXFP8 weight
+  // scales are one buffer range of EL*H*F/32 bytes, below 2^32
+  if ((int64_t)held(p) * p->hidden * p->ffn >= (1ll << 37)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 

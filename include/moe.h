@@ -125,8 +125,10 @@ typedef enum { MOE_OP_DISPATCH = 0, MOE_OP_GROUPED_GEMM = 1, MOE_OP_LAYER = 2 } 
 /*
  * Problem shape.  Limits: 0 <= M, M*k < 2^31; H and F multiples of 64 in
  * [64, 65536]; 1 <= E <= 512; 1 <= k <= min(E, 16); S >= 1; S*EL <= 1024
- * (S*EL <= 1023 when EL < E); R*max(H,F) < 2^31 and EL*H*F < 2^31 (32-bit
- * element offsets).
+ * (S*EL <= 1023 when EL < E); R*max(H,F) < 2^31 (32-bit element offsets
+ * into the per-pair buffers) and EL*H*F < 2^37 (weights are addressed per
+ * expert with 64-bit offsets; the MXFP8 weight scales are one range of
+ * EL*H*F/32 bytes).  Beyond these, MOE_ERR_UNSUPPORTED.
  * dtype is the type of x, the weights, X_perm and Hact: MOE_DTYPE_BF16
  * (fp32 accumulation), MOE_DTYPE_F32, or MOE_DTYPE_BF16_MXFP8 (Hact and
  * W_down MXFP8, the rest bf16; F a multiple of 128).  Logits, weights of the top-k and Y

@@ -332,7 +332,13 @@ typedef struct {
  *   given.
  * The fused kernel needs its whole grid resident (one workgroup per CU):
  * opts->grid above that returns MOE_ERR_UNSUPPORTED; n_mover >= grid returns
- * MOE_ERR_INVALID_ARGUMENT.  If a bounded device wait runs out, the kernel
+ * MOE_ERR_INVALID_ARGUMENT.  Residency is checked against the device, not
+ * against other work: a fused call running beside other kernels that hold
+ * CUs (another stream, another fused call) can have workgroups wait for
+ * ones that cannot start, until the bounded waits end it with
+ * MOE_ERR_DEVICE_TIMEOUT.  Run the fused path alone on the device, or with
+ * opts->grid at most the CUs it may have; the kernel chain has no such
+ * requirement.  If a bounded device wait runs out, the kernel
  * stops early and records MOE_ERR_DEVICE_TIMEOUT in the workspace; read it
  * with moe_debug_device_status.
  */

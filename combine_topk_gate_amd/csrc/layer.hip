@@ -148,32 +148,80 @@ __device__ int block_claim(int32_t* counter, int* lds_word) {
 }
 
 // out[t, columns of chunk c] for tokens [t0, t1) (t1 - t0 <= kCombineTokens).
-// The tokens' row indices and weights are staged in LDS; each thread then
-// owns one 4-column group and walks the tokens 8 at a time, so 8 * k row
-// loads per thread are in flight.
-__device__ void combine_chunk(const FusedArgs& a, int c, int64_t t0, int64_t t1, int* rows_lds, float* w_lds) {
+// The tokens' held slots (row index and weight, in slot order; a row outside
+// [0, M k) is a pair of an expert not held here) are compacted in LDS, with
+// their count per token.  Each thread then owns one 4-column group and walks
+// the tokens 16 at a time, two held slots per step: the 32 row loads of a
+// step are all issued before any is used, and a group takes as many steps
+// as its tokens' largest count needs (one load at a time per thread left a
+// combine item ~4x slower than the memory allows).  Per element the
+// arithmetic is combine_group's: from zero, held slots in order, one fmaf
+// each.
+__device__ void combine_chunk(const FusedArgs& a, int c, int64_t t0, int64_t t1, int* rows_lds, float* w_lds,
+                              int* cnt_lds) {
   const int n0 = c * kChunkTiles * kL1Cols;
   const int n1 = min(a.H, n0 + kChunkTiles * kL1Cols);
   const int groups = (n1 - n0) / 4;
   const int nt = (int)(t1 - t0), k = a.k;
+  const uint64_t R = (uint64_t)(a.M * k);
   for (int i = threadIdx.x; i < nt * k; i += kGemmThreads) {
     rows_lds[i] = a.f2s[t0 * k + i];
     w_lds[i] = a.topk_w[t0 * k + i];
   }
   __syncthreads();
-  constexpr int U = 8;
+  if (threadIdx.x < nt) {  // in place: the write index never passes the read index
+    const int i = threadIdx.x;
+    int n = 0;
+    for (int j = 0; j < k; ++j) {
+      const int32_t row = rows_lds[i * k + j];
+      if ((uint64_t)(int64_t)row >= R) continue;
+      rows_lds[i * k + n] = row;
+      w_lds[i * k + n] = w_lds[i * k + j];
+      ++n;
+    }
+    cnt_lds[i] = n;
+  }
+  __syncthreads();
+  constexpr int U = 16;
   for (int q = threadIdx.x; q < groups; q += kGemmThreads) {
     const int64_t n = n0 + 4 * q;
     for (int i0 = 0; i0 < nt; i0 += U) {
-      float4 o[U];
+      int hmax = 0;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int i = min(i0 + u, nt - 1);
-        o[u] = combine_group(a.y, w_lds + i * k, rows_lds + i * k, k, a.H, n, a.M * k);
+      for (int u = 0; u < U; ++u) hmax = max(hmax, cnt_lds[min(i0 + u, nt - 1)]);
+      hmax = uniform(hmax);  // the same LDS values in every lane
+      float4 acc[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int h0 = 0; h0 < hmax; h0 += 2) {
+        float4 v[2][U];
+        float wv[2][U];
+        bool has[2][U];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const int i = min(i0 + u, nt - 1);
+            has[h][u] = h0 + h < cnt_lds[i];
+            const int32_t row = has[h][u] ? rows_lds[i * k + h0 + h] : 0;
+            wv[h][u] = has[h][u] ? w_lds[i * k + h0 + h] : 0.f;
+            v[h][u] = has[h][u] ? *reinterpret_cast<const float4*>(a.y + (int64_t)row * a.H + n)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+          }
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            if (!has[h][u]) continue;
+            acc[u].x = fmaf(wv[h][u], v[h][u].x, acc[u].x);
+            acc[u].y = fmaf(wv[h][u], v[h][u].y, acc[u].y);
+            acc[u].z = fmaf(wv[h][u], v[h][u].z, acc[u].z);
+            acc[u].w = fmaf(wv[h][u], v[h][u].w, acc[u].w);
+          }
       }
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        if (i0 + u < nt) store_out(a.out, (t0 + i0 + u) * a.H + n, o[u]);
+        if (i0 + u < nt) store_out(a.out, (t0 + i0 + u) * a.H + n, acc[u]);
     }
   }
   __syncthreads();
@@ -185,6 +233,7 @@ __global__ __launch_bounds__(kGemmThreads) void fused_layer_kernel(FusedArgs a) 
   __shared__ int lds_word;
   __shared__ int comb_rows[kCombineTokens * 16];
   __shared__ float comb_w[kCombineTokens * 16];
+  __shared__ int comb_cnt[kCombineTokens];
 
   const int MT = build_tile_table(a.offsets, a.G, kTileRows, tl);
   const int nt0 = (a.F + kL0Cols - 1) / kL0Cols;
@@ -198,6 +247,7 @@ __global__ __launch_bounds__(kGemmThreads) void fused_layer_kernel(FusedArgs a) 
   const int CB = (int)((a.M + kCombineTokens - 1) / kCombineTokens);  // combine items per chunk
   const bool dedicated = a.n_mover > 0;
   auto chunk_width = [&](int c) { return min(kChunkTiles, nt1 - c * kChunkTiles); };
+  auto chunk_items = [&](int c) { return MT * chunk_width(c); };  // queue entries of chunk c's Layer1 tiles
   // reordering check: items permuted inside their section (Layer0 tiles,
   // one chunk's Layer1 tiles, one chunk's combine items); waits still
   // target earlier sections only
@@ -209,16 +259,16 @@ __global__ __launch_bounds__(kGemmThreads) void fused_layer_kernel(FusedArgs a) 
       const int v = block_claim(mover_q, &lds_word);
       if (v >= nc * CB) return;
       const int c = v / CB, tb = shuffled(s_cb, v - c * CB);
-      if (!block_wait(chunkdone + c, MT * chunk_width(c), a.status, limit, &lds_word)) return;
+      if (!block_wait(chunkdone + c, chunk_items(c), a.status, limit, &lds_word)) return;
       combine_chunk(a, c, (int64_t)tb * kCombineTokens, min(a.M, (int64_t)(tb + 1) * kCombineTokens), comb_rows,
-                    comb_w);
+                    comb_w, comb_cnt);
     }
   }
 
   // the single ordered queue of the other workgroups
   const int T0 = MT * nt0;
   int total = T0;
-  for (int c = 0; c < nc; ++c) total += MT * chunk_width(c) + ((dedicated || c == 0) ? 0 : CB);
+  for (int c = 0; c < nc; ++c) total += chunk_items(c) + ((dedicated || c == 0) ? 0 : CB);
   if (!dedicated) total += CB;
   const int W = gridDim.x - a.n_mover;
   const int xcd_slots = W / kXcds > 0 ? W / kXcds : 1;
@@ -264,7 +314,7 @@ __global__ __launch_bounds__(kGemmThreads) void fused_layer_kernel(FusedArgs a) 
     int comb_chunk = -1;
     for (; chunk <= nc; ++chunk) {
       if (chunk < nc) {
-        const int n = MT * chunk_width(chunk);
+        const int n = chunk_items(chunk);
         if (u < n) {
           is_tile = true;
           break;
@@ -280,7 +330,7 @@ __global__ __launch_bounds__(kGemmThreads) void fused_layer_kernel(FusedArgs a) 
       }
     }
     if (is_tile) {
-      const int ui = shuffled(make_shuffle(a.shuffle, MT * chunk_width(chunk)), u);
+      const int ui = shuffled(make_shuffle(a.shuffle, chunk_items(chunk)), u);
       const TileCoord c = tile_coord(ui, a.G, chunk_width(chunk), kTileRows, xcd_slots, (int64_t)kTileRows * a.F * 2, tl);
       if (!block_wait(l0done + c.mt, nt0, a.status, limit, &lds_word)) return;
       ga.a = reinterpret_cast<const __bf16*>(a.hact);
@@ -292,10 +342,10 @@ __global__ __launch_bounds__(kGemmThreads) void fused_layer_kernel(FusedArgs a) 
       bf16_gemm_row_tile<1>(ga, c.g, tl.seg_start[c.g], tl.seg_rows[c.g], c.m0, chunk * kChunkTiles + c.nt, lds);
       block_signal(chunkdone + chunk, 1);
     } else if (comb_chunk >= 0) {
-      if (!block_wait(chunkdone + comb_chunk, MT * chunk_width(comb_chunk), a.status, limit, &lds_word)) return;
+      if (!block_wait(chunkdone + comb_chunk, chunk_items(comb_chunk), a.status, limit, &lds_word)) return;
       const int tb = shuffled(s_cb, u);
       combine_chunk(a, comb_chunk, (int64_t)tb * kCombineTokens, min(a.M, (int64_t)(tb + 1) * kCombineTokens),
-                    comb_rows, comb_w);
+                    comb_rows, comb_w, comb_cnt);
     }
   }
 }

@@ -238,6 +238,24 @@ def test_edge_case_full_parity(edge):
     assert status == 0 and torch.equal(out, ref["out"])
 
 
+@pytest.mark.parametrize("n_mover", [0, 4])
+@pytest.mark.parametrize("edge", [e for e in EDGE if EDGE[e].get("dtype", "bf16") == "bf16"])
+def test_edge_case_fused_equals_chain(edge, n_mover):
+    """The fused kernel forced on every bf16 edge case (slots of experts not
+    held, k from 1 to 16, one token, empty experts and segments, 1024
+    segments), its combine items in the shared queue and on 4 dedicated
+    workgroups: bitwise the unsplit chain's output, which the case above
+    pins to the oracle."""
+    kw = dict(EDGE[edge])
+    bias = kw.pop("bias", None)
+    cfg, d = _edge_inputs(**kw, bias=bias)
+    g = upload(d)
+    print(f"[fused edge] {edge} n_mover={n_mover}", flush=True)
+    out, _, status = run_layer(cfg, g, n_mover=n_mover, gather=1)
+    assert status == 0
+    assert torch.equal(out, run_chain(cfg, g, gemm_ws=False)["out"])
+
+
 @pytest.mark.parametrize("edge", SPLIT_EDGES)
 def test_split_path_runs_and_is_deterministic(edge):
     """These shapes take the layer-1 split (a grid of one partial round, long

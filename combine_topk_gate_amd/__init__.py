@@ -248,7 +248,7 @@ def moe_layer(p, x, logits, src_block, w_gate, w_up, w_down, out, ws, aux: dict 
 
 def moe_layer_ex(p, x, logits, src_block, w_gate, w_up, w_down, epi, out, ws, aux: dict | None = None,
                  n_mover: int = -1, grid: int = 0, fused: int = 1, spin_limit: int = 0,
-              gather: int = -1, stream=None):
+                 gather: int = -1, stream=None):
     a = None
     if aux:
         a = LayerAux(**{k: (v.data_ptr() if v is not None else None) for k, v in aux.items()})

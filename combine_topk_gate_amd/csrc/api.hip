@@ -417,21 +417,22 @@ moe_status_t moe_layer_ex(const moe_problem_t* p, const void* x, const float* lo
     if (st == MOE_OK && p->num_src_blocks > 1) st = check_range(src_block, M, 0, p->num_src_blocks, s);
     if (st != MOE_OK) return st;
   }
-  // cleared with a fill kernel rather than a memset node, so that the call
-  // can be captured into a HIP graph
-  hipError_t e = launch_fill_i32(status, 1, 0, s);
-  if (e != hipSuccess) return MOE_ERR_HIP;
+  // zeroed by kernels rather than memset nodes, so that the call can be
+  // captured into a HIP graph
+  hipError_t e;
   if (M == 0) {
     // nothing routed: counts and offsets are all zero
-    e = launch_fill_i32(counts, G, 0, s);
+    e = launch_fill_i32(status, 1, 0, s);
+    if (e == hipSuccess) e = launch_fill_i32(counts, G, 0, s);
     if (e == hipSuccess) e = launch_fill_i32(offsets, G + 1, 0, s);
     return hip_status(e);
   }
-  e = launch_route(logits, M, p->num_experts, p->topk, idx, w, s);
-  if (e != hipSuccess) return MOE_ERR_HIP;
   const bool fused = o.fused != 0 && p->dtype == MOE_DTYPE_BF16 && movers >= 0;
+  // Layer0 of the fused kernel gathers its token rows from x unless the
+  // caller asks for the X_perm copy (o.gather == 0)
+  const bool gather = o.gather != 0;
+  FusedArgs fa;
   if (fused) {
-    FusedArgs fa;
     fa.M = M;
     fa.H = p->hidden;
     fa.F = p->ffn;
@@ -439,9 +440,6 @@ moe_status_t moe_layer_ex(const moe_problem_t* p, const void* x, const float* lo
     fa.k = p->topk;
     fa.G = G;
     fa.x = x;
-    // Layer0 gathers its token rows from x unless the caller asks for the
-    // X_perm copy (o.gather == 0)
-    const bool gather = o.gather != 0;
     fa.x_perm = gather ? nullptr : xp;
     fa.w_gate = w_gate;
     fa.w_up = w_up;
@@ -460,8 +458,15 @@ moe_status_t moe_layer_ex(const moe_problem_t* p, const void* x, const float* lo
     fa.n_mover = movers;
     fa.spin_limit = o.spin_limit;
     fa.shuffle = debug_shuffle();
-    moe_status_t fs = fused_check(fa, cus);
+    // checked before anything is launched
+    const moe_status_t fs = fused_check(fa, cus);
     if (fs != MOE_OK) return fs;
+  }
+  // the route kernel also clears the status word and (fused) the ready counters
+  e = launch_route(logits, M, p->num_experts, p->topk, idx, w, s, status, 1, fused ? fa.flags : nullptr,
+                   fused ? fused_flag_words(M, p->hidden, p->topk, G) : 0);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  if (fused) {
     // gathering, the kernel reads token rows straight from x and X_perm is
     // produced only when the caller asks for it
     e = launch_dispatch(plan_of(p), idx, src, counts, offsets, s2f, f2s, x, (int64_t)p->hidden * elem_bytes(p),

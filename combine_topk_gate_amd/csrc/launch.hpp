@@ -10,8 +10,12 @@
 
 namespace moe {
 
+// clear0 / clear1 (n0 / n1 words, null for none): words the kernel's first
+// block sets to zero, for kernels launched after it (the layer call's status
+// word and the fused kernel's ready counters), instead of a fill launch each.
 hipError_t launch_route(const float* logits, int64_t M, int E, int k, int32_t* topk_idx, float* topk_w,
-                        hipStream_t s);
+                        hipStream_t s, int32_t* clear0 = nullptr, int n0 = 0, int32_t* clear1 = nullptr,
+                        int n1 = 0);
 
 // Dispatch: segment bookkeeping (per-chunk histograms, bases, stable ranks)
 // and the copy of token rows to their sorted positions.  Pairs of experts

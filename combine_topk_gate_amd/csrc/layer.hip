@@ -584,10 +584,14 @@ moe_status_t fused_check(const FusedArgs& a, int cus) {
   return MOE_OK;
 }
 
+int fused_flag_words(int64_t M, int H, int k, int G) {
+  const FusedGeom f = fused_geom(M, H, k, G);
+  return f.mt_max + f.nc + kQueueWords;
+}
+
+// a.flags (fused_flag_words of them) must be zero: cleared on the stream
+// before this launch
 hipError_t launch_fused_layer(const FusedArgs& a, hipStream_t s) {
-  const FusedGeom f = fused_geom(a.M, a.H, a.k, a.G);
-  hipError_t e = launch_fill_i32(a.flags, (int64_t)f.mt_max + f.nc + kQueueWords, 0, s);
-  if (e != hipSuccess) return e;
   fused_layer_kernel<<<a.grid, kGemmThreads, 0, s>>>(a);
   return hipGetLastError();
 }

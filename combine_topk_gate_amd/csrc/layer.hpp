@@ -37,6 +37,10 @@ struct FusedArgs {
 
 size_t fused_ws_bytes(int64_t M, int H, int F, int E, int k, int S);
 int fused_mt_max(int64_t M, int H, int k, int G);
+// Words of the ready counters and queue counters at FusedArgs::flags; they
+// must be zero when the fused kernel starts (the layer call's route kernel
+// clears them).
+int fused_flag_words(int64_t M, int H, int k, int G);
 // EL: experts held (E when all are).  kTableUnusable: MOE_TUNING_TABLE names
 // a file that cannot be read or parsed.
 constexpr int kTableUnusable = -2;

@@ -85,10 +85,24 @@ __device__ __forceinline__ void topk_merge_partner(float (&vals)[KMAX], int (&id
   }
 }
 
+// Words the caller needs zero before the kernels that follow (the layer
+// call's status word and the fused kernel's ready counters): block 0 clears
+// them, which saves a launch per range.
+struct ClearRanges {
+  int32_t* p0 = nullptr;
+  int n0 = 0;
+  int32_t* p1 = nullptr;
+  int n1 = 0;
+};
+
 template <int KMAX>
 __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float* __restrict__ logits, int64_t M, int E,
                                                                    int k, int32_t* __restrict__ topk_idx,
-                                                                   float* __restrict__ topk_w) {
+                                                                   float* __restrict__ topk_w, ClearRanges clr) {
+  if (blockIdx.x == 0) {
+    for (int i = threadIdx.x; i < clr.n0; i += kRouteThreads) clr.p0[i] = 0;
+    for (int i = threadIdx.x; i < clr.n1; i += kRouteThreads) clr.p1[i] = 0;
+  }
   const int q = threadIdx.x % kLanesPerToken;
   const int64_t t = (int64_t)blockIdx.x * (kRouteThreads / kLanesPerToken) + threadIdx.x / kLanesPerToken;
   const bool valid = t < M;  // whole 16-lane groups share `valid`
@@ -133,20 +147,25 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float* 
 }
 
 hipError_t launch_route(const float* logits, int64_t M, int E, int k, int32_t* topk_idx, float* topk_w,
-                        hipStream_t s) {
+                        hipStream_t s, int32_t* clear0, int n0, int32_t* clear1, int n1) {
   if (M == 0) return hipSuccess;
+  ClearRanges clr;
+  clr.p0 = clear0;
+  clr.n0 = clear0 ? n0 : 0;
+  clr.p1 = clear1;
+  clr.n1 = clear1 ? n1 : 0;
   const int64_t per_block = kRouteThreads / kLanesPerToken;
   const dim3 grid((unsigned)((M + per_block - 1) / per_block)), block(kRouteThreads);
   if (k <= 1)
-    route_topk_kernel<1><<<grid, block, 0, s>>>(logits, M, E, k, topk_idx, topk_w);
+    route_topk_kernel<1><<<grid, block, 0, s>>>(logits, M, E, k, topk_idx, topk_w, clr);
   else if (k <= 2)
-    route_topk_kernel<2><<<grid, block, 0, s>>>(logits, M, E, k, topk_idx, topk_w);
+    route_topk_kernel<2><<<grid, block, 0, s>>>(logits, M, E, k, topk_idx, topk_w, clr);
   else if (k <= 4)
-    route_topk_kernel<4><<<grid, block, 0, s>>>(logits, M, E, k, topk_idx, topk_w);
+    route_topk_kernel<4><<<grid, block, 0, s>>>(logits, M, E, k, topk_idx, topk_w, clr);
   else if (k <= 8)
-    route_topk_kernel<8><<<grid, block, 0, s>>>(logits, M, E, k, topk_idx, topk_w);
+    route_topk_kernel<8><<<grid, block, 0, s>>>(logits, M, E, k, topk_idx, topk_w, clr);
   else
-    route_topk_kernel<16><<<grid, block, 0, s>>>(logits, M, E, k, topk_idx, topk_w);
+    route_topk_kernel<16><<<grid, block, 0, s>>>(logits, M, E, k, topk_idx, topk_w, clr);
   return hipGetLastError();
 }
 
